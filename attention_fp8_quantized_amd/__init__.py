@@ -1,0 +1,256 @@
+"""Python binding of libfa8attn.so (FP8-e4m3 paged-KV attention for gfx950).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+torch supplies device memory (``data_ptr``) and the stream
+(``torch.cuda.current_stream()``); nothing here computes on tensor values.
+If the library is missing the import of this module still works, but every
+call raises ``RuntimeError`` (there is no fallback path).
+
+Names follow the C ABI in include/fa8attn.h:
+    cache_write, decode_num_splits, decode_workspace_bytes,
+    decode_attention, prefill_kv_tile, prefill_attention
+"""
+
+import ctypes
+import os
+
+__all__ = [
+    "FA8_F32", "FA8_BF16", "FA8_E4M3", "BLOCK_SIZE", "Fa8Error", "library_path",
+    "load", "cache_write", "decode_num_splits", "decode_workspace_bytes",
+    "decode_attention", "prefill_kv_tile", "prefill_attention", "new_cache",
+    "new_decode_workspace",
+]
+
+FA8_F32, FA8_BF16, FA8_E4M3 = 0, 1, 2
+BLOCK_SIZE = 16
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path():
+    return os.path.join(_HERE, "libfa8attn.so")
+
+
+class Fa8Error(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"fa8attn status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+_VP, _I32, _I64, _F32, _SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                              ctypes.c_float, ctypes.c_size_t)
+
+_SIGNATURES = {
+    "fa8_cache_write": (_I32, [_VP, _VP, _I32, _I64, _I32, _I32, _VP, _VP, _VP, _VP,
+                               _I32, _I64, _VP]),
+    "fa8_decode_num_splits": (_I32, [_I32, _I32, _I32, _I32]),
+    "fa8_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
+    "fa8_decode_attention": (_I32, [_VP, _I32, _I32, _VP, _I32, _I64, _I32, _I32, _VP,
+                                    _I32, _VP, _I32, _VP, _VP, _F32, _I32, _I32, _VP,
+                                    _VP, _SZ, _VP]),
+    "fa8_prefill_kv_tile": (_I32, [_I32]),
+    "fa8_prefill_attention": (_I32, [_VP, _VP, _I32, _I32, _I32, _VP, _I64, _I32, _I32,
+                                     _VP, _I32, _VP, _VP, _VP, _VP, _F32, _I32, _I32,
+                                     _VP, _VP]),
+    "fa8_status_string": (ctypes.c_char_p, [_I32]),
+    "fa8_last_error": (ctypes.c_char_p, []),
+}
+
+
+def load():
+    """Load libfa8attn.so once and return the ctypes handle (raises if absent)."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is not built: run `python -m attention_fp8_quantized_amd.build` "
+                "(there is no fallback implementation)")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(status):
+    if status != 0:
+        lib = load()
+        raise Fa8Error(status, lib.fa8_last_error().decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _require(t, name, dtype=None, device=None, ndim=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _cache_dtype(cache):
+    torch = _torch()
+    if cache.dtype == torch.uint8:
+        return FA8_E4M3
+    if cache.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return FA8_BF16
+    raise ValueError("cache must be uint8 (e4m3 codes) or bfloat16")
+
+
+def new_cache(num_blocks, num_kv_heads, head_dim, cache_dtype="e4m3", device="cuda"):
+    """Allocate a paged cache tensor [num_blocks][H_kv][2][16][head_dim]."""
+    torch = _torch()
+    dt = torch.uint8 if cache_dtype == "e4m3" else torch.bfloat16
+    return torch.empty((num_blocks, num_kv_heads, 2, BLOCK_SIZE, head_dim),
+                       dtype=dt, device=device)
+
+
+def cache_write(k, v, slot_mapping, k_scale, v_scale, cache):
+    """Quantise (e4m3 cache) or round (bf16 cache) k/v [N][H_kv][D] into the
+    paged cache at ``slot_mapping`` (int64 [N]; negative = skip)."""
+    torch = _torch()
+    _require(cache, "cache", ndim=5)
+    dev = cache.device
+    nb, hkv, two, bs, d = cache.shape
+    if two != 2 or bs != BLOCK_SIZE:
+        raise ValueError("cache must be [num_blocks][H_kv][2][16][D]")
+    _require(k, "k", device=dev, ndim=3)
+    _require(v, "v", dtype=k.dtype, device=dev, ndim=3)
+    if k.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("k/v must be float32 or bfloat16")
+    if tuple(k.shape[1:]) != (hkv, d) or k.shape != v.shape:
+        raise ValueError(f"k/v must be [N][{hkv}][{d}]")
+    _require(slot_mapping, "slot_mapping", dtype=torch.int64, device=dev, ndim=1)
+    if slot_mapping.shape[0] != k.shape[0]:
+        raise ValueError("slot_mapping must have one entry per row")
+    cdt = _cache_dtype(cache)
+    if cdt == FA8_E4M3:
+        for s, nm in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+            _require(s, nm, dtype=torch.float32, device=dev, ndim=1)
+            if s.shape[0] != hkv:
+                raise ValueError(f"{nm} must have {hkv} entries")
+    lib = load()
+    _check(lib.fa8_cache_write(
+        _ptr(k), _ptr(v), FA8_BF16 if k.dtype == torch.bfloat16 else FA8_F32,
+        k.shape[0], hkv, d, _ptr(slot_mapping),
+        _ptr(k_scale) if cdt == FA8_E4M3 else None,
+        _ptr(v_scale) if cdt == FA8_E4M3 else None,
+        _ptr(cache), cdt, nb, _stream(cache)))
+
+
+def decode_num_splits(batch, num_kv_heads, max_seq_len, window=0):
+    return int(load().fa8_decode_num_splits(batch, num_kv_heads, max_seq_len, window))
+
+
+def decode_workspace_bytes(batch, num_q_heads, head_dim, num_splits):
+    return int(load().fa8_decode_workspace_bytes(batch, num_q_heads, head_dim, num_splits))
+
+
+def new_decode_workspace(nbytes, device="cuda"):
+    """Zero-filled decode workspace of ``nbytes`` (the library needs it zeroed
+    once; every decode call leaves it reusable)."""
+    torch = _torch()
+    return torch.zeros(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+def decode_attention(q, cache, block_table, seq_lens, k_scale, v_scale, sm_scale,
+                     max_seq_len, window=0, num_splits=0, out=None, workspace=None):
+    """One decode step. q bf16 [B][H_q][D] -> out fp32 [B][H_q][D].
+
+    ``max_seq_len`` is a host-side upper bound of ``seq_lens`` (sizes the
+    grid).  ``workspace`` (uint8 device tensor from ``new_decode_workspace``)
+    is allocated here when not given; pass one to keep the call
+    allocation-free."""
+    torch = _torch()
+    _require(cache, "cache", ndim=5)
+    dev = cache.device
+    nb, hkv, _, _, d = cache.shape
+    _require(q, "q", dtype=torch.bfloat16, device=dev, ndim=3)
+    B, hq, dq = q.shape
+    if dq != d:
+        raise ValueError("q head_dim does not match the cache")
+    _require(block_table, "block_table", dtype=torch.int32, device=dev, ndim=2)
+    _require(seq_lens, "seq_lens", dtype=torch.int32, device=dev, ndim=1)
+    if block_table.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("block_table / seq_lens must have one row per sequence")
+    cdt = _cache_dtype(cache)
+    if cdt == FA8_E4M3:
+        _require(k_scale, "k_scale", dtype=torch.float32, device=dev, ndim=1)
+        _require(v_scale, "v_scale", dtype=torch.float32, device=dev, ndim=1)
+    lib = load()
+    splits = num_splits or decode_num_splits(B, hkv, int(max_seq_len), int(window))
+    need = decode_workspace_bytes(B, hq, d, splits)
+    if workspace is None:
+        workspace = new_decode_workspace(need, dev)
+    else:
+        _require(workspace, "workspace", device=dev)
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=torch.float32, device=dev)
+    else:
+        _require(out, "out", dtype=torch.float32, device=dev, ndim=3)
+    _check(lib.fa8_decode_attention(
+        _ptr(q), B, hq, _ptr(cache), cdt, nb, hkv, d, _ptr(block_table),
+        block_table.shape[1], _ptr(seq_lens), int(max_seq_len),
+        _ptr(k_scale) if cdt == FA8_E4M3 else None,
+        _ptr(v_scale) if cdt == FA8_E4M3 else None,
+        float(sm_scale), int(window), int(splits), _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(cache)))
+    return out
+
+
+def prefill_kv_tile(head_dim):
+    return int(load().fa8_prefill_kv_tile(head_dim))
+
+
+def prefill_attention(q, cu_q_lens, cache, block_table, seq_lens, q_scale, k_scale,
+                      v_scale, sm_scale, max_q_len, window=0, accum_mode=1, out=None):
+    """Causal FP8 prefill. q bf16 [T][H_q][D] (packed by ``cu_q_lens``) ->
+    out fp32 [T][H_q][D].  ``seq_lens`` count the context including the
+    chunk; ``q_scale`` is a 1-element fp32 device tensor."""
+    torch = _torch()
+    _require(cache, "cache", dtype=torch.uint8, ndim=5)
+    dev = cache.device
+    nb, hkv, _, _, d = cache.shape
+    _require(q, "q", dtype=torch.bfloat16, device=dev, ndim=3)
+    T, hq, dq = q.shape
+    if dq != d:
+        raise ValueError("q head_dim does not match the cache")
+    _require(cu_q_lens, "cu_q_lens", dtype=torch.int32, device=dev, ndim=1)
+    B = cu_q_lens.shape[0] - 1
+    _require(block_table, "block_table", dtype=torch.int32, device=dev, ndim=2)
+    _require(seq_lens, "seq_lens", dtype=torch.int32, device=dev, ndim=1)
+    for s, nm in ((q_scale, "q_scale"), (k_scale, "k_scale"), (v_scale, "v_scale")):
+        _require(s, nm, dtype=torch.float32, device=dev, ndim=1)
+    if out is None:
+        out = torch.empty((T, hq, d), dtype=torch.float32, device=dev)
+    else:
+        _require(out, "out", dtype=torch.float32, device=dev, ndim=3)
+    lib = load()
+    _check(lib.fa8_prefill_attention(
+        _ptr(q), _ptr(cu_q_lens), B, hq, int(max_q_len), _ptr(cache), nb, hkv, d,
+        _ptr(block_table), block_table.shape[1], _ptr(seq_lens), _ptr(q_scale),
+        _ptr(k_scale), _ptr(v_scale), float(sm_scale), int(window), int(accum_mode),
+        _ptr(out), _stream(cache)))
+    return out

@@ -1,0 +1,261 @@
+// C ABI of libfa8attn.so (declared in include/fa8attn.h): argument checks,
+// split heuristic, workspace sizing, error strings, then the launches.
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/fa8attn.h"
+#include "fa8_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fa8_status fail(fa8_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+fa8_status fail(fa8_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+fa8_status ok() {
+  g_last_error.clear();
+  return FA8_OK;
+}
+
+fa8_status hip_fail(hipError_t e, const char* what) {
+  return fail(FA8_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
+bool group_ok(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  static thread_local int cached_dev = -1, cached_cus = 0;
+  if (dev == cached_dev) return cached_cus;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0) {
+    (void)hipGetLastError();
+    cus = 256;
+  }
+  cached_dev = dev;
+  cached_cus = cus;
+  return cus;
+}
+
+// Pages one decode workgroup may have to visit for the longest sequence.
+int decode_pages_max(int max_seq_len, int window) {
+  if (max_seq_len <= 0) return 0;
+  const int visible = window > 0 ? std::min(window, max_seq_len) : max_seq_len;
+  // a window that does not start on a page boundary spans one extra page
+  return (visible + FA8_BLOCK_SIZE - 1) / FA8_BLOCK_SIZE + (window > 0 ? 1 : 0);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa8_status_string(int32_t status) {
+  switch (status) {
+    case FA8_OK: return "ok";
+    case FA8_EINVAL: return "invalid argument";
+    case FA8_EUNSUPPORTED: return "unsupported configuration";
+    case FA8_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* fa8_last_error(void) { return g_last_error.c_str(); }
+
+fa8_status fa8_cache_write(const void* k, const void* v, int32_t in_dtype,
+                           int64_t n_tokens, int32_t num_kv_heads, int32_t head_dim,
+                           const int64_t* slot_mapping, const float* k_scale,
+                           const float* v_scale, void* cache, int32_t cache_dtype,
+                           int64_t num_blocks, void* stream) {
+  if (n_tokens < 0) return fail(FA8_EINVAL, "cache_write: n_tokens < 0");
+  if (in_dtype != FA8_F32 && in_dtype != FA8_BF16)
+    return fail(FA8_EINVAL, "cache_write: in_dtype must be FA8_F32 or FA8_BF16");
+  if (cache_dtype != FA8_E4M3 && cache_dtype != FA8_BF16)
+    return fail(FA8_EINVAL, "cache_write: cache_dtype must be FA8_E4M3 or FA8_BF16");
+  if (num_kv_heads <= 0) return fail(FA8_EINVAL, "cache_write: num_kv_heads must be > 0");
+  if (!head_dim_ok(head_dim))
+    return fail(FA8_EUNSUPPORTED, "cache_write: head_dim %d not in {64,128,256}", head_dim);
+  if (num_blocks < 0) return fail(FA8_EINVAL, "cache_write: num_blocks < 0");
+  if (n_tokens == 0) return ok();
+  if (!k || !v || !slot_mapping || !cache)
+    return fail(FA8_EINVAL, "cache_write: null k, v, slot_mapping or cache");
+  if (cache_dtype == FA8_E4M3 && (!k_scale || !v_scale))
+    return fail(FA8_EINVAL, "cache_write: FA8_E4M3 cache needs k_scale and v_scale");
+  const hipError_t e = fa8::launch_cache_write(
+      k, v, in_dtype == FA8_BF16, n_tokens, num_kv_heads, head_dim, slot_mapping,
+      k_scale, v_scale, cache, cache_dtype == FA8_E4M3,
+      reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "cache_write launch");
+  return ok();
+}
+
+int32_t fa8_decode_num_splits(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len,
+                              int32_t window) {
+  const int pages = decode_pages_max(max_seq_len, window);
+  if (batch <= 0 || num_kv_heads <= 0 || pages <= 0) return 1;
+  // Aim for about four 4-wave workgroups per CU, and at least 8 pages
+  // (two per wave) in every split.
+  const int cus = device_cu_count();
+  const long target_wgs = 4L * cus;
+  long splits = (target_wgs + (long)batch * num_kv_heads - 1) / ((long)batch * num_kv_heads);
+  const long by_pages = (pages + 7) / 8;
+  if (splits > by_pages) splits = by_pages;
+  if (splits < 1) splits = 1;
+  if (splits > 1024) splits = 1024;
+  return (int32_t)splits;
+}
+
+size_t fa8_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t num_splits) {
+  if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || num_splits <= 0) return 0;
+  return fa8::decode_workspace_bytes(batch, num_q_heads, head_dim, num_splits);
+}
+
+fa8_status fa8_decode_attention(const void* q, int32_t batch, int32_t num_q_heads,
+                                const void* cache, int32_t cache_dtype, int64_t num_blocks,
+                                int32_t num_kv_heads, int32_t head_dim,
+                                const int32_t* block_table, int32_t max_blocks_per_seq,
+                                const int32_t* seq_lens, int32_t max_seq_len,
+                                const float* k_scale, const float* v_scale, float sm_scale,
+                                int32_t window, int32_t num_splits, float* out,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch < 0) return fail(FA8_EINVAL, "decode: batch < 0");
+  if (num_q_heads <= 0 || num_kv_heads <= 0)
+    return fail(FA8_EINVAL, "decode: head counts must be > 0");
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(FA8_EINVAL, "decode: num_q_heads %d not a multiple of num_kv_heads %d",
+                num_q_heads, num_kv_heads);
+  if (!group_ok(num_q_heads / num_kv_heads))
+    return fail(FA8_EUNSUPPORTED, "decode: query heads per KV head %d not in {1,2,4,8,16}",
+                num_q_heads / num_kv_heads);
+  if (!head_dim_ok(head_dim))
+    return fail(FA8_EUNSUPPORTED, "decode: head_dim %d not in {64,128,256}", head_dim);
+  if (cache_dtype != FA8_E4M3 && cache_dtype != FA8_BF16)
+    return fail(FA8_EINVAL, "decode: cache_dtype must be FA8_E4M3 or FA8_BF16");
+  if (max_seq_len < 0 || max_blocks_per_seq < 0 || num_blocks < 0)
+    return fail(FA8_EINVAL, "decode: negative size");
+  if ((int64_t)max_blocks_per_seq * FA8_BLOCK_SIZE < max_seq_len)
+    return fail(FA8_EINVAL, "decode: max_blocks_per_seq*16 < max_seq_len");
+  if (!(std::isfinite(sm_scale)))
+    return fail(FA8_EINVAL, "decode: sm_scale must be finite");
+  if (num_splits < 0 || num_splits > fa8::kDecodeMaxSplits)
+    return fail(FA8_EINVAL, "decode: num_splits must be in 0..%d", fa8::kDecodeMaxSplits);
+  if (batch == 0) return ok();
+  if (!q || !cache || !block_table || !seq_lens || !out || !workspace)
+    return fail(FA8_EINVAL, "decode: null pointer argument");
+  if (cache_dtype == FA8_E4M3 && (!k_scale || !v_scale))
+    return fail(FA8_EINVAL, "decode: FA8_E4M3 cache needs k_scale and v_scale");
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return fail(FA8_EINVAL, "decode: workspace must be 16-byte aligned");
+
+  const int S = num_splits > 0 ? num_splits
+                               : fa8_decode_num_splits(batch, num_kv_heads, max_seq_len, window);
+  const size_t need = fa8::decode_workspace_bytes(batch, num_q_heads, head_dim, S);
+  if (workspace_bytes < need)
+    return fail(FA8_EINVAL, "decode: workspace has %zu bytes, %zu needed for %d splits",
+                workspace_bytes, need, S);
+
+  fa8::DecodeParams p{};
+  p.q = reinterpret_cast<const uint16_t*>(q);
+  p.cache = reinterpret_cast<const uint8_t*>(cache);
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  fa8::decode_workspace_carve(workspace, batch, num_q_heads, head_dim, S, &p.ws_count,
+                              &p.ws_o, &p.ws_m, &p.ws_l);
+  p.out = out;
+  p.batch = batch;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.max_blocks = max_blocks_per_seq;
+  p.num_splits = S;
+  const int pages = decode_pages_max(max_seq_len, window);
+  p.pages_per_split = pages > 0 ? (pages + S - 1) / S : 1;
+  p.window = window > 0 ? window : 0;
+  p.fp8 = cache_dtype == FA8_E4M3 ? 1 : 0;
+  p.sm_scale = sm_scale;
+  const hipError_t e =
+      fa8::launch_decode(p, cache_dtype == FA8_E4M3, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return ok();
+}
+
+int32_t fa8_prefill_kv_tile(int32_t head_dim) {
+  if (!head_dim_ok(head_dim)) return 0;
+  return fa8::prefill_kv_tile(head_dim);
+}
+
+fa8_status fa8_prefill_attention(const void* q, const int32_t* cu_q_lens, int32_t batch,
+                                 int32_t num_q_heads, int32_t max_q_len, const void* cache,
+                                 int64_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                                 const int32_t* block_table, int32_t max_blocks_per_seq,
+                                 const int32_t* seq_lens, const float* q_scale,
+                                 const float* k_scale, const float* v_scale, float sm_scale,
+                                 int32_t window, int32_t accum_mode, float* out,
+                                 void* stream) {
+  if (batch < 0 || max_q_len < 0 || num_blocks < 0 || max_blocks_per_seq < 0)
+    return fail(FA8_EINVAL, "prefill: negative size");
+  if (num_q_heads <= 0 || num_kv_heads <= 0)
+    return fail(FA8_EINVAL, "prefill: head counts must be > 0");
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(FA8_EINVAL, "prefill: num_q_heads %d not a multiple of num_kv_heads %d",
+                num_q_heads, num_kv_heads);
+  if (!head_dim_ok(head_dim))
+    return fail(FA8_EUNSUPPORTED, "prefill: head_dim %d not in {64,128,256}", head_dim);
+  if (accum_mode != 0 && accum_mode != 1)
+    return fail(FA8_EINVAL, "prefill: accum_mode must be 0 or 1");
+  if (!(std::isfinite(sm_scale)))
+    return fail(FA8_EINVAL, "prefill: sm_scale must be finite");
+  if (batch == 0 || max_q_len == 0) return ok();
+  if (!q || !cu_q_lens || !cache || !block_table || !seq_lens || !q_scale || !k_scale ||
+      !v_scale || !out)
+    return fail(FA8_EINVAL, "prefill: null pointer argument");
+
+  fa8::PrefillParams p{};
+  p.q = reinterpret_cast<const uint16_t*>(q);
+  p.cu_q_lens = cu_q_lens;
+  p.cache = reinterpret_cast<const uint8_t*>(cache);
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.q_scale = q_scale;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.out = out;
+  p.batch = batch;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.max_blocks = max_blocks_per_seq;
+  p.max_q_len = max_q_len;
+  p.window = window > 0 ? window : 0;
+  p.accum_mode = accum_mode;
+  p.sm_scale = sm_scale;
+  const hipError_t e = fa8::launch_prefill(p, reinterpret_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported)
+    return fail(FA8_EUNSUPPORTED, "prefill: configuration not built");
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,135 @@
+// Cache write: quantise new K/V rows with their per-KV-head scale and scatter
+// them into 16-token pages.
+//
+// [BLOG] "Kernel and vLLM improvements / Per-Head Scales": the cache-write
+// kernel takes an array of scales, one per KV head.  [EXPLAINER] "FP8
+// combines value and scale": the value is divided by its scale before it is
+// quantised.  Rounding is nearest-even with saturation at +-448.
+//
+// One thread produces one 16-byte chunk of one cached row: 16 e4m3 codes or
+// 8 bf16 values.  Threads of a block walk (token, head, chunk) with the chunk
+// fastest, so input reads are contiguous; blockIdx.y picks K (0) or V (1).
+// The work is a single HBM-bound pass.  The fp32 quotient x / scale must be
+// correctly rounded: this file is built without fast-math and with
+// -fhip-fp32-correctly-rounded-divide-sqrt.
+
+#include "fa8_device.hpp"
+#include "fa8_internal.hpp"
+
+namespace fa8 {
+
+template <bool kInBf16>
+__device__ __forceinline__ void load_inputs(const void* src, int64_t elem, float* x,
+                                            int n) {
+  if constexpr (kInBf16) {
+    const uint4* p = reinterpret_cast<const uint4*>(
+        reinterpret_cast<const uint16_t*>(src) + elem);
+    for (int i = 0; i < n / 8; ++i) {
+      uint4 w = p[i];
+      uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+      for (int j = 0; j < 4; ++j) {
+        x[i * 8 + 2 * j] = bf16_lo(ws[j]);
+        x[i * 8 + 2 * j + 1] = bf16_hi(ws[j]);
+      }
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(
+        reinterpret_cast<const float*>(src) + elem);
+    for (int i = 0; i < n / 4; ++i) {
+      float4 w = p[i];
+      x[i * 4 + 0] = w.x;
+      x[i * 4 + 1] = w.y;
+      x[i * 4 + 2] = w.z;
+      x[i * 4 + 3] = w.w;
+    }
+  }
+}
+
+template <bool kInBf16, bool kFp8Cache>
+__global__ __launch_bounds__(256) void cache_write_kernel(
+    const void* __restrict__ k, const void* __restrict__ v, int64_t n_tokens,
+    int num_kv_heads, int head_dim, const int64_t* __restrict__ slot_mapping,
+    const float* __restrict__ k_scale, const float* __restrict__ v_scale,
+    uint8_t* __restrict__ cache) {
+  constexpr int kElemBytes = kFp8Cache ? 1 : 2;
+  constexpr int kPerThread = 16 / kElemBytes;  // elements per 16-byte chunk
+  const int chunks_per_row = head_dim / kPerThread;
+  const int64_t total = n_tokens * num_kv_heads * chunks_per_row;
+  const int which = blockIdx.y;  // 0 = K, 1 = V
+  const void* src = which ? v : k;
+  const float* scale = which ? v_scale : k_scale;
+
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(t % chunks_per_row);
+    const int64_t rest = t / chunks_per_row;
+    const int h = (int)(rest % num_kv_heads);
+    const int64_t n = rest / num_kv_heads;
+    const int64_t slot = slot_mapping[n];
+    if (slot < 0) continue;  // padding row
+
+    float x[kPerThread];
+    load_inputs<kInBf16>(src, (n * num_kv_heads + h) * head_dim + c * kPerThread,
+                         x, kPerThread);
+
+    uint32_t packed[4];
+    if constexpr (kFp8Cache) {
+      const float s = scale[h];
+      for (int w = 0; w < 4; ++w) {
+        uint32_t word = 0;
+        for (int j = 0; j < 4; ++j) {
+          const float y = x[w * 4 + j] / s;  // correctly rounded fp32 quotient
+          word |= e4m3_encode(y) << (8 * j);
+        }
+        packed[w] = word;
+      }
+    } else {
+      for (int w = 0; w < 4; ++w)
+        packed[w] = bf16_bits(x[2 * w]) | (bf16_bits(x[2 * w + 1]) << 16);
+    }
+
+    const int64_t blk = slot / kBlockSize;
+    const int row = (int)(slot % kBlockSize);
+    const int64_t off =
+        ((((blk * num_kv_heads + h) * 2 + which) * kBlockSize + row) * head_dim +
+         (int64_t)c * kPerThread) * kElemBytes;
+    *reinterpret_cast<uint4*>(cache + off) =
+        make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  }
+}
+
+hipError_t launch_cache_write(const void* k, const void* v, bool in_bf16,
+                              int64_t n_tokens, int num_kv_heads, int head_dim,
+                              const int64_t* slot_mapping, const float* k_scale,
+                              const float* v_scale, void* cache, bool fp8_cache,
+                              hipStream_t stream) {
+  const int per = fp8_cache ? 16 : 8;
+  const int64_t total = n_tokens * num_kv_heads * (head_dim / per);
+  const int threads = 256;
+  int64_t blocks = (total + threads - 1) / threads;
+  if (blocks > 65535) blocks = 65535;  // grid-stride loop covers the rest
+  dim3 grid((unsigned)blocks, 2);
+  uint8_t* c = reinterpret_cast<uint8_t*>(cache);
+  if (fp8_cache) {
+    if (in_bf16)
+      hipLaunchKernelGGL((cache_write_kernel<true, true>), grid, threads, 0, stream,
+                         k, v, n_tokens, num_kv_heads, head_dim, slot_mapping,
+                         k_scale, v_scale, c);
+    else
+      hipLaunchKernelGGL((cache_write_kernel<false, true>), grid, threads, 0, stream,
+                         k, v, n_tokens, num_kv_heads, head_dim, slot_mapping,
+                         k_scale, v_scale, c);
+  } else {
+    if (in_bf16)
+      hipLaunchKernelGGL((cache_write_kernel<true, false>), grid, threads, 0, stream,
+                         k, v, n_tokens, num_kv_heads, head_dim, slot_mapping,
+                         k_scale, v_scale, c);
+    else
+      hipLaunchKernelGGL((cache_write_kernel<false, false>), grid, threads, 0, stream,
+                         k, v, n_tokens, num_kv_heads, head_dim, slot_mapping,
+                         k_scale, v_scale, c);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fa8

@@ -1,0 +1,106 @@
+// Device helpers shared by the fa8attn kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa8 {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kBlockSize = 16;
+
+// ---------------------------------------------------------------------------
+// e4m3 encoding (OCP E4M3: bias 7, max 448, S.1111.111 = NaN), written as
+// integer operations on the float32 bit pattern so the result is exact:
+// round-to-nearest-even, saturation at +-448 (also for +-inf), NaN -> 0x7F
+// with the input's sign, sign of zero kept.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+  const uint32_t bits = __float_as_uint(y);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const uint32_t a = bits & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a > 0x7F800000u) {
+    code = 0x7Fu;                        // NaN
+  } else if (a >= 0x43E00000u) {
+    code = 0x7Eu;                        // |y| >= 448 (incl. inf): saturate
+  } else if (a < 0x3C800000u) {
+    // |y| < 2^-6: subnormal codes m * 2^-9, m = rne(|y| * 2^9) in 0..8
+    // (scaling by 2^9 is exact; rintf rounds half to even)
+    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  } else {
+    // normal: keep 3 of the 23 mantissa bits with ties-to-even, then rebias
+    // the exponent from 127 to 7; a mantissa carry moves into the exponent
+    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    code = (r >> 20) - (120u << 3);
+  }
+  return code | sign;
+}
+
+// fp32 -> bf16 bits, round-to-nearest-even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) | 0x40u) & 0xFFFFu;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Two e4m3 codes (bytes 0,1 of w, or 2,3 when kHi) -> two fp32 values (exact).
+template <bool kHi>
+__device__ __forceinline__ f32x2 e4m3x2_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(w, kHi);
+}
+
+// Two e4m3 codes -> packed bf16 pair (exact: bf16 holds every e4m3 value).
+template <bool kHi>
+__device__ __forceinline__ bf16x2 e4m3x2_to_bf16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHi);
+}
+
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(bf16x2, w);
+}
+
+// acc + a.x*b.x + a.y*b.y  (products of bf16 are exact in fp32)
+__device__ __forceinline__ float dot2_bf16(bf16x2 a, bf16x2 b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(a, b, acc, false);
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane sums over aligned groups of N lanes (N = 1..64).  Steps 1 and 2
+// use DPP quad permutes, 4 and 8 the row half-mirror / mirror (after the
+// lower steps every lane of a quad / half-row holds the same partial, so a
+// mirror pairs each lane with a lane of the other half), 16 and 32 fall back
+// to a bpermute shuffle.
+// ---------------------------------------------------------------------------
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl,
+                                         0xF, 0xF, false));
+}
+
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  if constexpr (N >= 4) x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) x += dpp<0x141>(x);  // row_half_mirror
+  if constexpr (N >= 16) x += dpp<0x140>(x); // row_mirror
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) {
+  return __builtin_amdgcn_exp2f(x);  // v_exp_f32; exp2(-inf) = 0
+}
+
+}  // namespace fa8

@@ -1,0 +1,63 @@
+// Host-side launch entry points of the fa8attn kernels (internal; the public
+// C ABI is include/fa8attn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa8 {
+
+hipError_t launch_cache_write(const void* k, const void* v, bool in_bf16,
+                              int64_t n_tokens, int num_kv_heads, int head_dim,
+                              const int64_t* slot_mapping, const float* k_scale,
+                              const float* v_scale, void* cache, bool fp8_cache,
+                              hipStream_t stream);
+
+struct DecodeParams {
+  const uint16_t* q;          // bf16 [B][Hq][D]
+  const uint8_t* cache;       // [nb][Hkv][2][16][D] elements
+  const int32_t* block_table; // [B][max_blocks]
+  const int32_t* seq_lens;    // [B]
+  const float* k_scale;       // [Hkv]
+  const float* v_scale;       // [Hkv]
+  int* ws_count;              // arrival counters, zero between calls
+  float* ws_o;                // [B][Hq][S][D]
+  float* ws_m;                // [B][Hq][S]  (log2 domain)
+  float* ws_l;                // [B][Hq][S]
+  float* out;                 // [B][Hq][D]
+  int batch, num_q_heads, num_kv_heads, head_dim, max_blocks;
+  int num_splits, pages_per_split, window, fp8;
+  float sm_scale;
+};
+
+// Decode workspace layout for `splits` splits (each array 16-byte aligned):
+// int32 arrival counters [B][Hq] (zero before the first call; every call
+// leaves them zero), then fp32 o_part [B][Hq][S][D], m [B][Hq][S] and
+// l [B][Hq][S].
+constexpr int kDecodeMaxSplits = 1024;
+size_t decode_workspace_bytes(int batch, int num_q_heads, int head_dim, int splits);
+void decode_workspace_carve(void* ws, int batch, int num_q_heads, int head_dim, int splits,
+                            int** count, float** o, float** m, float** l);
+
+hipError_t launch_decode(const DecodeParams& p, bool fp8_cache, hipStream_t stream);
+
+struct PrefillParams {
+  const uint16_t* q;          // bf16 [Tq][Hq][D]
+  const int32_t* cu_q_lens;   // [B+1]
+  const uint8_t* cache;       // e4m3 [nb][Hkv][2][16][D]
+  const int32_t* block_table; // [B][max_blocks]
+  const int32_t* seq_lens;    // [B] (context incl. the chunk)
+  const float* q_scale;       // [1]
+  const float* k_scale;       // [Hkv]
+  const float* v_scale;       // [Hkv]
+  float* out;                 // [Tq][Hq][D]
+  int batch, num_q_heads, num_kv_heads, head_dim, max_blocks, max_q_len;
+  int window, accum_mode;
+  float sm_scale;
+};
+
+int prefill_kv_tile(int head_dim);
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+
+}  // namespace fa8

@@ -1,0 +1,198 @@
+/*
+ * fa8attn: attention over an FP8-e4m3 paged KV cache with per-KV-head scales,
+ * for AMD CDNA4 (gfx950 / MI355X).  C ABI of libfa8attn.so.
+ *
+ * Pages the operations follow (cited by title and section):
+ *   [BLOG]      "State of FP8 KV-Cache and Attention Quantization in vLLM"
+ *               (vLLM Blog, 2026-04-22).
+ *   [EXPLAINER] "KV Cache量子化とは？FP8でLLMの同時実行数を増やす前に測ること"
+ *               (vasteelab.pages.dev, 2026-10-07).
+ * The e4m3 bits follow the OCP OFP8 E4M3 definition (bias 7, max 448, no
+ * infinity, S.1111.111 = NaN), which the pages name but do not spell out.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every pointer argument is a DEVICE pointer owned by the caller (normally
+ *   the storage of a torch tensor).  The library allocates nothing and keeps
+ *   no device state; scratch space for decode is a caller-sized workspace.
+ * - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *   NULL = the null stream).  No call synchronises with the host or copies
+ *   between host and device, so every call can be captured in a HIP graph.
+ * - Paged cache layout, one allocation per layer:
+ *       cache[num_blocks][num_kv_heads][2][16][head_dim]
+ *   index 2 is 0 = K, 1 = V; 16 tokens per block (page).  A token with slot
+ *   id t lives in block t / 16, row t % 16.  Element type: one byte per
+ *   element (e4m3 code) for FA8_E4M3, two (bf16 bits) for FA8_BF16.  The
+ *   K rows and the V rows of one (block, head) are each 16*head_dim elements
+ *   of contiguous memory.
+ * - Scales: k_scale[num_kv_heads], v_scale[num_kv_heads] fp32 in device
+ *   memory, one per KV head ([BLOG] "Kernel and vLLM improvements /
+ *   Per-Head Scales").  A per-tensor scale is the case of equal entries.
+ *   Dequantised value = scale * decode(code).  Scales must be finite and
+ *   positive (not checked on the device).
+ * - Errors: host-side checks return FA8_EINVAL (bad argument) or
+ *   FA8_EUNSUPPORTED (valid but not built, e.g. head_dim 96) before anything
+ *   is launched; a failed launch returns FA8_EHIP.  fa8_last_error() gives a
+ *   message for the calling thread.  Indices that only the device sees
+ *   (slot ids, block ids, sequence lengths) are preconditions: out-of-range
+ *   values are undefined behaviour.
+ */
+#ifndef FA8ATTN_H
+#define FA8ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA8_OK = 0,
+  FA8_EINVAL = 1,
+  FA8_EUNSUPPORTED = 2,
+  FA8_EHIP = 3
+} fa8_status;
+
+typedef enum { FA8_F32 = 0, FA8_BF16 = 1, FA8_E4M3 = 2 } fa8_dtype;
+
+#define FA8_BLOCK_SIZE 16
+
+/*
+ * Quantise and scatter new K/V rows into the paged cache.
+ * [BLOG] "Kernel and vLLM improvements / Per-Head Scales" (the cache-write
+ * kernel takes one scale per KV head); [EXPLAINER] "FP8 combines value and
+ * scale" (values are divided by their scale before quantisation).
+ *
+ *   k, v          [n_tokens][num_kv_heads][head_dim], in_dtype FA8_F32 or
+ *                 FA8_BF16, row-major, contiguous.
+ *   slot_mapping  int64 [n_tokens]; a negative slot skips the row (padding).
+ *                 Slots must be < num_blocks*16 and pairwise distinct.
+ *   cache         see the layout above; cache_dtype FA8_E4M3 or FA8_BF16.
+ * FA8_E4M3: code = e4m3(fl32(x / scale[h])) with the fp32 quotient
+ *   correctly rounded, then round-to-nearest-even, saturation at +-448
+ *   (also for +-inf), NaN -> 0x7F|sign, sign of zero kept.
+ * FA8_BF16: the bf16 rounding (nearest-even) of x; scales are not read and
+ *   may be NULL (layers kept in BF16, [BLOG] "Skipping layers").
+ * n_tokens == 0 is a no-op.
+ */
+fa8_status fa8_cache_write(const void* k, const void* v, int32_t in_dtype,
+                           int64_t n_tokens, int32_t num_kv_heads,
+                           int32_t head_dim, const int64_t* slot_mapping,
+                           const float* k_scale, const float* v_scale,
+                           void* cache, int32_t cache_dtype, int64_t num_blocks,
+                           void* stream);
+
+/*
+ * Split-KV decode: number of context splits the library picks for a batch
+ * (host-only heuristic; depends on the device's CU count).  `window` as in
+ * fa8_decode_attention.  Always >= 1.
+ */
+int32_t fa8_decode_num_splits(int32_t batch, int32_t num_kv_heads,
+                              int32_t max_seq_len, int32_t window);
+
+/*
+ * Bytes of device workspace fa8_decode_attention needs for `num_splits`
+ * splits: one int32 arrival counter per (sequence, query head), then per
+ * (sequence, query head, split) one unnormalised partial output row
+ * (head_dim fp32) plus its running maximum and denominator (2 fp32).
+ */
+size_t fa8_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
+                                  int32_t head_dim, int32_t num_splits);
+
+/*
+ * One decode step of grouped-query attention over the paged cache.
+ * [BLOG] "Performance benchmarks / Single-request benchmark" (the kernel
+ * reads the FP8 cache natively, rescaling its online softmax as it goes);
+ * [EXPLAINER] "Memory reduction is not speed" (quantised values are
+ * dequantised inside the attention kernel, not in a separate pass).
+ *
+ *   q            bf16 [batch][num_q_heads][head_dim]; query head hq reads
+ *                KV head hq / (num_q_heads / num_kv_heads).
+ *   block_table  int32 [batch][max_blocks_per_seq] physical block ids.
+ *   seq_lens     int32 [batch]; the query is token seq_lens[b]-1, whose K/V
+ *                must already be in the cache.  0 gives a zero output row.
+ *   max_seq_len  host upper bound of seq_lens (sizes the grid only).
+ *   k_scale/v_scale  per-KV-head scales (read for FA8_E4M3 only).
+ *   sm_scale     softmax scale (usually 1/sqrt(head_dim)).
+ *   window       > 0: attend to the last `window` keys (the query's own
+ *                token included); <= 0: the whole context.
+ *   num_splits   context splits, 0..1024; 0 = fa8_decode_num_splits(...).
+ *   out          fp32 [batch][num_q_heads][head_dim]
+ *                out = sum_j softmax(sm_scale * q.K_j) * V_j.
+ *   workspace    >= fa8_decode_workspace_bytes(batch, num_q_heads,
+ *                head_dim, splits) bytes, 16-byte aligned.  It must be
+ *                zero-filled before its first use; every call leaves its
+ *                arrival counters at zero again, so a workspace can be reused
+ *                without clearing.  Calls that share a workspace must be
+ *                ordered on one stream.
+ * Supported: head_dim in {64, 128, 256}; num_q_heads / num_kv_heads in
+ * {1, 2, 4, 8, 16}; cache_dtype FA8_E4M3 or FA8_BF16.
+ */
+fa8_status fa8_decode_attention(const void* q, int32_t batch,
+                                int32_t num_q_heads, const void* cache,
+                                int32_t cache_dtype, int64_t num_blocks,
+                                int32_t num_kv_heads, int32_t head_dim,
+                                const int32_t* block_table,
+                                int32_t max_blocks_per_seq,
+                                const int32_t* seq_lens, int32_t max_seq_len,
+                                const float* k_scale, const float* v_scale,
+                                float sm_scale, int32_t window,
+                                int32_t num_splits, float* out,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
+ * Width (keys) of the KV tiles fa8_prefill_attention visits, in ascending,
+ * tile-aligned order from key 0.  It is part of the numeric contract: the
+ * probabilities are quantised to e4m3 against the running maximum reached
+ * after each tile.  Returns 0 for an unsupported head_dim.
+ */
+int32_t fa8_prefill_kv_tile(int32_t head_dim);
+
+/*
+ * Causal FP8 prefill over the paged cache with two-level accumulation.
+ * [BLOG] "Introduction" (QK and Score*V both run in e4m3); "Kernel and vLLM
+ * improvements / Two-level accumulation" (partial P*V sums are flushed into
+ * true FP32 registers); "Query Quantization Fusion" (Q is quantised with a
+ * per-tensor scale right before attention).
+ *
+ *   q          bf16 [total_q][num_q_heads][head_dim], sequences packed;
+ *              sequence b owns rows cu_q_lens[b] .. cu_q_lens[b+1]-1.
+ *   cu_q_lens  int32 [batch+1], cu_q_lens[0] = 0.
+ *   max_q_len  host upper bound of the per-sequence query counts.
+ *   seq_lens   int32 [batch]: context length INCLUDING this chunk; the
+ *              chunk's queries sit at positions seq_len - q_len .. seq_len-1
+ *              and their K/V must already be in the cache.
+ *   q_scale    fp32 [1] device: q8 = e4m3(fl32(q / q_scale)).
+ *   window     as in decode, counted from each query's own position.
+ *   accum_mode 1 = two-level (MFMA sums each KV tile into a zeroed fp32
+ *              register tile, then O = alpha*O + tile in fp32; default);
+ *              0 = one-level (MFMA accumulates into the rescaled O).
+ *   out        fp32 [total_q][num_q_heads][head_dim].
+ * Per row and KV tile t (width fa8_prefill_kv_tile): running max m_t,
+ * p = exp(s - m_t) in fp32, P*V uses e4m3(p), the denominator the fp32 p.
+ * Supported: head_dim in {64, 128, 256}; cache_dtype FA8_E4M3 only.
+ */
+fa8_status fa8_prefill_attention(const void* q, const int32_t* cu_q_lens,
+                                 int32_t batch, int32_t num_q_heads,
+                                 int32_t max_q_len, const void* cache,
+                                 int64_t num_blocks, int32_t num_kv_heads,
+                                 int32_t head_dim, const int32_t* block_table,
+                                 int32_t max_blocks_per_seq,
+                                 const int32_t* seq_lens, const float* q_scale,
+                                 const float* k_scale, const float* v_scale,
+                                 float sm_scale, int32_t window,
+                                 int32_t accum_mode, float* out, void* stream);
+
+/* Static English name of a status code. */
+const char* fa8_status_string(int32_t status);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* fa8_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA8ATTN_H */

@@ -1,0 +1,138 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+that include/fa8attn.h declares, and rejects bad arguments on the host before
+anything is launched."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_fp8_quantized_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa8attn.h")
+
+EINVAL, EUNSUPPORTED = 1, 2
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa8_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.library_path()):
+        pytest.fail("libfa8attn.so is not built (python -m attention_fp8_quantized_amd.build)")
+    return fa.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert {"fa8_cache_write", "fa8_decode_attention", "fa8_prefill_attention"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in fa._SIGNATURES, f"binding lacks {n}"
+
+
+def test_status_strings(lib):
+    assert lib.fa8_status_string(0) == b"ok"
+    assert lib.fa8_status_string(1) == b"invalid argument"
+    assert lib.fa8_status_string(99) == b"unknown status"
+
+
+def test_kv_tile_contract(lib):
+    for d in (64, 128, 256):
+        t = lib.fa8_prefill_kv_tile(d)
+        assert t > 0 and t % 16 == 0
+    assert lib.fa8_prefill_kv_tile(96) == 0
+
+
+def test_workspace_size(lib):
+    # counters B*Hq int32, o_part B*Hq*S*D fp32, m and l B*Hq*S fp32 each;
+    # every array starts on a 16-byte boundary
+    assert lib.fa8_decode_workspace_bytes(1, 32, 128, 64) == \
+        32 * 4 + 32 * 64 * 128 * 4 + 2 * 32 * 64 * 4
+    assert lib.fa8_decode_workspace_bytes(1, 1, 64, 1) == 16 + 256 + 16 + 16
+    assert lib.fa8_decode_workspace_bytes(0, 1, 64, 1) == 0
+
+
+def test_num_splits_bounds(lib):
+    assert lib.fa8_decode_num_splits(1, 8, 0, 0) == 1
+    s = lib.fa8_decode_num_splits(1, 8, 32768, 0)
+    assert 1 <= s <= 1024
+    # at least 8 pages per split
+    assert lib.fa8_decode_num_splits(1, 8, 64, 0) == 1
+    # a 128-token window never needs more than ceil(128/16)+1 pages
+    assert lib.fa8_decode_num_splits(8, 8, 20000, 128) <= 2
+
+
+def _p(x):
+    return ctypes.c_void_p(x)
+
+
+def test_cache_write_rejects_bad_arguments(lib):
+    fake = _p(0x1000)
+    # bad input dtype
+    assert lib.fa8_cache_write(fake, fake, 2, 1, 1, 64, fake, fake, fake, fake, 2, 1, None) == EINVAL
+    assert b"in_dtype" in lib.fa8_last_error()
+    # unsupported head_dim
+    assert lib.fa8_cache_write(fake, fake, 0, 1, 1, 96, fake, fake, fake, fake, 2, 1, None) == EUNSUPPORTED
+    # null pointers
+    assert lib.fa8_cache_write(None, fake, 0, 1, 1, 64, fake, fake, fake, fake, 2, 1, None) == EINVAL
+    # e4m3 cache without scales
+    assert lib.fa8_cache_write(fake, fake, 0, 1, 1, 64, fake, None, None, fake, 2, 1, None) == EINVAL
+    # n_tokens == 0 is a no-op (nothing launched)
+    assert lib.fa8_cache_write(None, None, 0, 0, 1, 64, None, None, None, None, 2, 0, None) == 0
+    assert lib.fa8_last_error() == b""
+
+
+def _decode(lib, **over):
+    fake = _p(0x1000)
+    a = dict(q=fake, B=1, Hq=8, cache=fake, cd=2, nb=4, Hkv=2, D=64, bt=fake, mb=4,
+             lens=fake, maxlen=64, ks=fake, vs=fake, sm=0.125, window=0, splits=1,
+             out=fake, ws=_p(0x2000), wsb=1 << 20, stream=None)
+    a.update(over)
+    return lib.fa8_decode_attention(a["q"], a["B"], a["Hq"], a["cache"], a["cd"], a["nb"],
+                                    a["Hkv"], a["D"], a["bt"], a["mb"], a["lens"], a["maxlen"],
+                                    a["ks"], a["vs"], a["sm"], a["window"], a["splits"],
+                                    a["out"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_decode_rejects_bad_arguments(lib):
+    assert _decode(lib, Hq=7) == EINVAL                      # not a multiple of H_kv
+    assert _decode(lib, Hq=6, Hkv=2) == EUNSUPPORTED         # G = 3
+    assert _decode(lib, D=96) == EUNSUPPORTED
+    assert _decode(lib, cd=0) == EINVAL
+    assert _decode(lib, maxlen=65) == EINVAL                 # 4 blocks hold 64 tokens
+    assert _decode(lib, wsb=100) == EINVAL
+    assert b"workspace" in lib.fa8_last_error()
+    assert _decode(lib, ws=_p(0x2004)) == EINVAL             # misaligned
+    assert _decode(lib, q=None) == EINVAL
+    assert _decode(lib, ks=None) == EINVAL                   # e4m3 needs scales
+    assert _decode(lib, sm=float("inf")) == EINVAL
+    assert _decode(lib, splits=-1) == EINVAL
+    assert _decode(lib, splits=1025) == EINVAL
+    assert _decode(lib, B=0) == 0                            # empty batch: no-op
+
+
+def test_prefill_rejects_bad_arguments(lib):
+    fake = _p(0x1000)
+
+    def call(**over):
+        a = dict(q=fake, cu=fake, B=1, Hq=8, mq=16, cache=fake, nb=4, Hkv=2, D=64, bt=fake,
+                 mb=4, lens=fake, qs=fake, ks=fake, vs=fake, sm=0.125, window=0, acc=1,
+                 out=fake)
+        a.update(over)
+        return lib.fa8_prefill_attention(a["q"], a["cu"], a["B"], a["Hq"], a["mq"], a["cache"],
+                                         a["nb"], a["Hkv"], a["D"], a["bt"], a["mb"], a["lens"],
+                                         a["qs"], a["ks"], a["vs"], a["sm"], a["window"],
+                                         a["acc"], a["out"], None)
+
+    assert call(Hq=7) == EINVAL
+    assert call(D=80) == EUNSUPPORTED
+    assert call(acc=2) == EINVAL
+    assert call(qs=None) == EINVAL
+    assert call(B=0) == 0

@@ -1,0 +1,144 @@
+"""GPU split-KV decode vs the fp64 oracle.
+
+Gate (every call): max |gpu - oracle| <= 2e-3 and relative L2 <= 1e-3 over
+the compared outputs.  The same bound is used at every context length from
+512 to 128k.  Large cases compare the query heads of a few KV heads (the
+oracle computes those heads exactly over the whole context); the GPU runs the
+full layer in the launch configuration the benchmark times (automatic split
+count).
+"""
+
+import numpy as np
+import pytest
+
+from _gpu_common import DecodeCase, assert_gate, log, metrics
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(case, what, **kw):
+    log(f"decode {what}")
+    got = case.run_gpu(**kw)
+    ref, qheads = case.oracle()
+    assert_gate(got[:, qheads], ref, what)
+    return got
+
+
+def test_single_layer_hd64_ctx512_unit_scales():
+    # 8 q / 2 KV heads, head_dim 64, 512 tokens in 32 pages, scales 1.0
+    c = DecodeCase(1, 8, 2, 64, [512], "e4m3", seed=1, scales="one")
+    _check(c, "hd64 ctx512 unit scales")
+
+
+@pytest.mark.parametrize("cd", ["e4m3", "bf16"])
+@pytest.mark.parametrize("ctx", [1024, 8192, 32768, 131072])
+def test_llama_shaped_layer(ctx, cd):
+    # 32 q / 8 KV heads, head_dim 128, outlier channels x20, absmax/448 scales
+    heads = None if ctx <= 32768 else [0, 5]
+    c = DecodeCase(1, 32, 8, 128, [ctx], cd, seed=2, outliers=True, oracle_heads=heads)
+    _check(c, f"llama-shaped ctx={ctx} {cd}")
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("cd", ["e4m3", "bf16"])
+def test_gqa_head_dims_ragged_batch(D, G, cd):
+    Hkv = 2
+    lens = [300, 0, 1, 17, 1000]
+    c = DecodeCase(len(lens), G * Hkv, Hkv, D, lens, cd, seed=10 + D + G)
+    got = _check(c, f"D={D} G={G} {cd} ragged")
+    assert np.all(got[1] == 0), "empty sequence must give zeros"
+
+
+@pytest.mark.parametrize("window", [1, 16, 100, 128, 513])
+@pytest.mark.parametrize("cd", ["e4m3", "bf16"])
+def test_sliding_window(window, cd):
+    lens = [1000, 37, 128, 129]
+    c = DecodeCase(len(lens), 16, 2, 64, lens, cd, seed=20 + window, window=window)
+    _check(c, f"window={window} {cd}")
+
+
+def test_split_count_invariance():
+    c = DecodeCase(2, 32, 8, 128, [5000, 3333], "e4m3", seed=30)
+    ref, qheads = c.oracle()
+    outs = {}
+    for s in [1, 2, 3, 7, 0, 64, 313]:
+        log(f"decode splits={s}")
+        outs[s] = c.run_gpu(num_splits=s)
+        assert_gate(outs[s][:, qheads], ref, f"splits={s}")
+    for s, o in outs.items():
+        ma, rl = metrics(o, outs[1])
+        assert rl < 2e-6, (s, rl)
+
+
+def test_page_permutation_invariance():
+    import torch
+    c = DecodeCase(1, 32, 8, 128, [4000], "e4m3", seed=31)
+    base = c.run_gpu()
+    # move every physical block to a new id and rewrite the table
+    nb = c.cache.shape[0]
+    perm = torch.from_numpy(np.random.default_rng(0).permutation(nb)).cuda()
+    moved = torch.empty_like(c.cache)
+    moved[perm] = c.cache
+    c.cache = moved
+    bt = c.bt.copy()
+    bt[bt >= 0] = perm.cpu().numpy()[bt[bt >= 0]]
+    c.bt_dev = torch.from_numpy(bt).cuda()
+    log("decode page permutation")
+    got = c.run_gpu()
+    np.testing.assert_array_equal(got, base)
+
+
+def test_uniform_scores_give_mean_of_v():
+    # q = 0: every visible token has weight 1/n, so out = mean of V-hat
+    from oracle import e4m3
+    c = DecodeCase(2, 8, 2, 128, [777, 64], "e4m3", seed=32, q_zero=True)
+    got = c.run_gpu()
+    at = 0
+    for b, L in enumerate(c.lens):
+        for hq in range(8):
+            h = hq // 4
+            codes = np.array([np.frombuffer(e4m3.encode(c.v[at + t, h] / c.vs[h]).tobytes(), np.uint8)
+                              for t in range(L)])
+            mean = e4m3.decode(codes).mean(axis=0) * np.float64(c.vs[h])
+            ma, rl = metrics(got[b, hq], mean)
+            assert ma < 1e-5 and rl < 1e-5, (b, hq, ma, rl)
+        at += L
+
+
+def test_loaded_decode_shape():
+    # 8 sequences of U{18000..22000} tokens, 32 q / 8 KV heads, head_dim 128
+    import workloads as W
+    lens = W.uniform_lengths(W.rng(3, 0, W.LENGTHS), 8, 18000, 22000)
+    c = DecodeCase(8, 32, 8, 128, lens, "e4m3", seed=3, oracle_heads=[3])
+    _check(c, "8 x ~20k loaded decode")
+
+
+@pytest.mark.parametrize("variant", ["full-fp8", "sw128-bf16", "sw128-fp8"])
+def test_hybrid_layers(variant):
+    # gpt-oss-20b-shaped: 64 q / 8 KV heads, head_dim 64, 8 x 20000 tokens
+    cd = "bf16" if "bf16" in variant else "e4m3"
+    window = 128 if variant.startswith("sw") else 0
+    heads = [1] if window == 0 else None
+    c = DecodeCase(8, 64, 8, 64, [20000] * 8, cd, seed=4, window=window, oracle_heads=heads)
+    _check(c, f"hybrid {variant}")
+
+
+def test_hd256_long_decode():
+    # 8 q / 1 KV head, head_dim 256, 128k context
+    c = DecodeCase(1, 8, 1, 256, [131072], "e4m3", seed=5)
+    _check(c, "hd256 ctx=131072")
+
+
+def test_argument_errors_raise():
+    import torch
+    import attention_fp8_quantized_amd as fa
+    c = DecodeCase(1, 8, 2, 64, [64], "e4m3", seed=6)
+    with pytest.raises(fa.Fa8Error):
+        # workspace far too small
+        fa.decode_attention(c.q_dev, c.cache, c.bt_dev, c.lens_dev, c.ks_dev, c.vs_dev,
+                            0.125, 64, workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    with pytest.raises(fa.Fa8Error):
+        # max_seq_len beyond what the block table can address
+        fa.decode_attention(c.q_dev, c.cache, c.bt_dev, c.lens_dev, c.ks_dev, c.vs_dev,
+                            0.125, 10 ** 6)
