@@ -112,15 +112,16 @@ int32_t fa8_decode_num_splits(int32_t batch, int32_t num_kv_heads, int32_t max_s
                               int32_t window) {
   const int pages = decode_pages_max(max_seq_len, window);
   if (batch <= 0 || num_kv_heads <= 0 || pages <= 0) return 1;
-  // Aim for about four 4-wave workgroups per CU, and at least 8 pages
-  // (two per wave) in every split.
+  // Aim for one workgroup per CU (a decode workgroup fills a CU's register
+  // file), and at least two pages per wave in every split.
   const int cus = device_cu_count();
-  const long target_wgs = 4L * cus;
+  const long target_wgs = cus;
   long splits = (target_wgs + (long)batch * num_kv_heads - 1) / ((long)batch * num_kv_heads);
-  const long by_pages = (pages + 7) / 8;
+  const long min_pages = 2L * fa8::kDecodeWaves;
+  const long by_pages = (pages + min_pages - 1) / min_pages;
   if (splits > by_pages) splits = by_pages;
   if (splits < 1) splits = 1;
-  if (splits > 1024) splits = 1024;
+  if (splits > fa8::kDecodeMaxSplits) splits = fa8::kDecodeMaxSplits;
   return (int32_t)splits;
 }
 

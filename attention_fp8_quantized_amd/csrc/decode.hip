@@ -7,125 +7,215 @@
 // not speed": dequantisation happens inside the attention kernel, in
 // registers, not as a separate pass back to high precision.
 //
-// Work decomposition (one workgroup per (split, KV head [x head group], seq)):
-//   * the context pages of a sequence are cut into `num_splits` contiguous
-//     page ranges; the NW waves of a workgroup take the pages of its range
-//     round-robin, one 16-token page at a time;
-//   * a page-head is 16 rows of D elements, i.e. 16*D*elem bytes of
-//     contiguous memory for K and again for V.  Each lane loads 16-byte
-//     chunks: LPT = D*elem/16 lanes cover one row, so one wave-wide load
-//     covers TPW = 64/LPT rows (a contiguous 1 KiB) and every global load is
-//     fully coalesced.  The next page is loaded while the current one is
-//     processed (register double buffer);
-//   * lanes of one row hold the same d-range of q for the GW query heads
-//     that share the KV head (GQA).  Partial q.k dots use v_dot2_f32_bf16 on
-//     bf16 pairs: e4m3 codes convert exactly to bf16 with one instruction per
-//     pair, bf16 cache rows are used as they are.  The LPT partials are summed
-//     with DPP lane permutes;
-//   * each group of LPT lanes (a "row slot") keeps its own online-softmax
-//     state (running max m and sum l in the log2 domain, fp32 output slice);
-//     slots are merged with shuffles at the end, waves through LDS, and the
-//     workgroup writes one unnormalised partial (o, m, l) per query head;
-//   * the last workgroup of a (sequence, head group) to finish merges the
-//     splits:  out = v_scale * sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+// Work decomposition: one workgroup of NW waves per (split, KV head [x head
+// group], sequence).
+//   * The visible pages of a sequence are cut into `num_splits` contiguous
+//     ranges; the waves of a workgroup take the pages of its range
+//     round-robin.  Each wave reads its block ids once (one lane per page)
+//     and keeps two pages in flight in a 3-deep register ring while it
+//     processes the third, so the block-table lookup never sits on the
+//     load path.
+//   * A page-head is 16 rows of D elements: 16*D*elem contiguous bytes for K
+//     and again for V.  A lane loads CB-byte chunks (16 bytes; 8 for e4m3
+//     with D = 64): LPT = D*elem/CB consecutive lanes cover a row, one
+//     wave-wide load covers TPW = 64/LPT consecutive rows, so every load
+//     instruction reads one contiguous span.  Each lane ends up with RPL
+//     rows of the page (same columns).
+//   * q . k: lanes of a row hold the same column range of q for the GW query
+//     heads that share the KV head (GQA).  e4m3 codes convert exactly to bf16
+//     pairs (one instruction per pair) and feed v_dot2_f32_bf16 with the bf16
+//     query (also exact); bf16 cache rows feed it directly.  The LPT partial
+//     sums are added across lanes with DPP.
+//   * online softmax in the log2 domain; each row slot (LPT lanes) keeps its
+//     own running max m, sum l and fp32 output columns, so nothing is
+//     exchanged between slots inside the loop.  Full pages take a branch
+//     without masking; the pages at the window start / sequence end mask.
+//   * p . v: e4m3 -- two rows of the same lane form a token pair; their codes
+//     are interleaved with v_perm_b32, converted to f16 pairs (exact) and
+//     multiplied with the pair of probabilities rounded to f16 by
+//     v_dot2_f32_f16 (fp32 accumulation).  bf16 -- rows convert to fp32 and
+//     use fp32 FMAs.
+//   * slots merge with shuffles, waves through LDS; each workgroup writes one
+//     unnormalised partial (o, m, l) per query head.  The workgroup that
+//     finishes last for its (sequence, head group) merges the splits:
+//        out = v_scale * sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
 // Scales are folded: k_scale into the score multiplier, v_scale into the
 // combine.  Empty splits carry m = -inf and weight 0; an all-empty row is 0.
 
+#include <type_traits>
+
 #include "fa8_device.hpp"
 #include "fa8_internal.hpp"
+
+#ifndef FA8_DECODE_F16_PV
+#define FA8_DECODE_F16_PV 1    // e4m3 p.v: f16 probability pairs + v_dot2_f32_f16
+#endif
 
 namespace fa8 {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kMaxSplits = kDecodeMaxSplits;
+// lazy-rescale threshold (log2 units): probabilities stay below 2^8, far
+// inside f16 range, and fp32 sums lose nothing
+constexpr float kLazy = 8.0f;
 
-// Merge the S split partials of GW query heads (run by one workgroup):
+template <int N>
+struct Chunk {
+  uint32_t w[N];
+};
+
+template <int N>
+__device__ __forceinline__ Chunk<N> load_chunk(const uint8_t* p) {
+  Chunk<N> c;
+  if constexpr (N == 4) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    c.w[0] = v.x; c.w[1] = v.y; c.w[2] = v.z; c.w[3] = v.w;
+  } else {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    c.w[0] = v.x; c.w[1] = v.y;
+  }
+  return c;
+}
+
+// Workspace traffic between workgroups uses agent-scope atomic loads and
+// stores: they are coherent across the chip's separate L2 caches without a
+// full-cache fence (a __threadfence() writes back / invalidates a whole L2).
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Merge the S split partials of GW query heads (run by the last workgroup):
 //   out = v_scale * sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-// Threads are laid out as (split row sr, 4-element column d4) so that many
-// splits are read at once with 16-byte loads; one pass covers RPP splits.
+// The maxima, the denominators and the first CH partial rows of every output
+// element are requested together, so the merge costs one memory round trip
+// whenever S <= CH * R.
 template <int D, int GW, int NW>
 __device__ __forceinline__ void combine_splits(const DecodeParams& p, int b, int h, int hq0) {
   constexpr int NT = 64 * NW;
-  constexpr int TPR = D / 4;          // threads per split row
-  constexpr int RPP = NT / TPR;       // split rows per pass
-  __shared__ float s_w[kMaxSplits];
-  __shared__ float s_red[NT];
-  __shared__ float4 s_acc[RPP][TPR];
+  constexpr int COLS = GW * D;                    // output elements
+  constexpr int R = NT >= COLS ? NT / COLS : 1;   // threads per output element
+  constexpr int CH = 16;                          // partial rows per thread per pass
+  __shared__ float s_m[GW][kMaxSplits];
+  __shared__ float s_l[GW][kMaxSplits];
+  __shared__ float s_mx[GW];
+  __shared__ float s_den[GW];
   const int S = p.num_splits;
   const int t = threadIdx.x;
-  const int sr = t / TPR;
-  const int d4 = t % TPR;
-  const float vsc = p.fp8 ? p.v_scale[h] : 1.0f;
-  for (int g = 0; g < GW; ++g) {
-    const size_t base = ((size_t)b * p.num_q_heads + hq0 + g) * S;
-    // M = max_s m_s
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const size_t base = ((size_t)b * p.num_q_heads + hq0) * S;   // row of (g=0, s=0)
+  // this thread's first output element (the loop below covers the rest)
+  const int col0 = t / R;
+  const int r = t % R;
+  float ov[CH];
+  if (col0 < COLS) {
+    const float* o = p.ws_o + (base + (size_t)(col0 / D) * S) * D + col0 % D;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int sp = r + i * R;
+      ov[i] = sp < S ? ld_agent(o + (size_t)sp * D) : 0.f;
+    }
+  }
+  for (int i = t; i < GW * S; i += NT) {
+    s_m[i / S][i % S] = ld_agent(p.ws_m + base + i);
+    s_l[i / S][i % S] = ld_agent(p.ws_l + base + i);
+  }
+  __syncthreads();
+  // per head: M, weights 2^(m_s - M) (in place of m) and the denominator
+  for (int g = wave; g < GW; g += NW) {
     float M = kNegInf;
-    for (int s = t; s < S; s += NT) M = fmaxf(M, p.ws_m[base + s]);
-    s_red[t] = M;
-    __syncthreads();
-    for (int w = NT / 2; w > 0; w /= 2) {
-      if (t < w) s_red[t] = fmaxf(s_red[t], s_red[t + w]);
-      __syncthreads();
-    }
-    M = s_red[0];
-    __syncthreads();
-    // split weights 2^(m_s - M) and the denominator
+    for (int sp = lane; sp < S; sp += 64) M = fmaxf(M, s_m[g][sp]);
+#pragma unroll
+    for (int x = 1; x < 64; x *= 2) M = fmaxf(M, __shfl_xor(M, x));
     float den = 0.f;
-    for (int s = t; s < S; s += NT) {
-      const float ms = p.ws_m[base + s];
-      const float f = (ms > kNegInf) ? fast_exp2(ms - M) : 0.f;
-      s_w[s] = f;
-      den += f * p.ws_l[base + s];
+    for (int sp = lane; sp < S; sp += 64) {
+      const float ms = s_m[g][sp];
+      const float f = (M > kNegInf && ms > kNegInf) ? fast_exp2(ms - M) : 0.f;
+      s_m[g][sp] = f;
+      den += f * s_l[g][sp];
     }
-    s_red[t] = den;
-    __syncthreads();
-    for (int w = NT / 2; w > 0; w /= 2) {
-      if (t < w) s_red[t] += s_red[t + w];
-      __syncthreads();
+#pragma unroll
+    for (int x = 1; x < 64; x *= 2) den += __shfl_xor(den, x);
+    if (lane == 0) {
+      s_mx[g] = M;
+      s_den[g] = den;
     }
-    den = s_red[0];
-    // numerator
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    const float4* o4 = reinterpret_cast<const float4*>(p.ws_o + base * D);
-    for (int s = sr; s < S; s += RPP) {
-      const float f = s_w[s];
-      const float4 v = o4[(size_t)s * TPR + d4];
-      acc.x += f * v.x;
-      acc.y += f * v.y;
-      acc.z += f * v.z;
-      acc.w += f * v.w;
-    }
-    s_acc[sr][d4] = acc;
-    __syncthreads();
-    if (t < TPR) {
-      float4 r = s_acc[0][t];
-      for (int q = 1; q < RPP; ++q) {
-        r.x += s_acc[q][t].x;
-        r.y += s_acc[q][t].y;
-        r.z += s_acc[q][t].z;
-        r.w += s_acc[q][t].w;
+  }
+  __syncthreads();
+  const float vsc = p.fp8 ? p.v_scale[h] : 1.0f;
+  for (int col = col0; col < COLS; col += NT / R) {
+    const int g = col / D;
+    const int d = col % D;
+    const float* o = p.ws_o + (base + (size_t)g * S) * D + d;
+    float acc = 0.f;
+    if (col == col0) {
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int sp = r + i * R;
+        if (sp < S) acc += s_m[g][sp] * ov[i];
       }
-      float4 res = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (M > kNegInf) {
-        const float sc = vsc / den;
-        res = make_float4(r.x * sc, r.y * sc, r.z * sc, r.w * sc);
-      }
-      reinterpret_cast<float4*>(p.out + ((size_t)b * p.num_q_heads + hq0 + g) * D)[t] = res;
+    } else {
+      for (int sp = r; sp < min(S, CH * R); sp += R) acc += s_m[g][sp] * ld_agent(o + (size_t)sp * D);
     }
-    __syncthreads();
+    for (int sp = r + CH * R; sp < S; sp += R) acc += s_m[g][sp] * ld_agent(o + (size_t)sp * D);
+#pragma unroll
+    for (int x = 1; x < R; x *= 2) acc += __shfl_xor(acc, x);
+    if (r == 0) {
+      const float res = s_mx[g] > kNegInf ? acc * (vsc / s_den[g]) : 0.f;
+      p.out[((size_t)b * p.num_q_heads + hq0 + g) * D + d] = res;
+    }
   }
 }
 
-template <int D, int GW, bool kFp8, int NW>
-__global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeParams p) {
-  constexpr int ES = kFp8 ? 1 : 2;          // bytes per cached element
-  constexpr int EPC = 16 / ES;              // elements per 16-byte lane chunk
-  constexpr int LPT = D / EPC;              // lanes per token row
-  constexpr int TPW = 64 / LPT;             // rows per wave-wide load
-  constexpr int RPL = kBlockSize / TPW;     // rows per lane per page half
+// Values of the lane `x` lanes away (x = 8: DPP rotate within a 16-lane row;
+// 16 / 32: permlane swaps), returned as the pair (value from the lower
+// partner, value from the upper partner) so that a symmetric merge needs no
+// select.  For x = 8 the pair is (own, partner).
+template <int X>
+__device__ __forceinline__ void lane_pair(float v, float& a, float& b) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  if constexpr (X == 8) {
+    a = v;
+    b = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, (int)u, 0x128, 0xF, 0xF, false));
+  } else if constexpr (X == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    a = __builtin_bit_cast(float, (uint32_t)r[0]);
+    b = __builtin_bit_cast(float, (uint32_t)r[1]);
+  } else {
+    static_assert(X == 32, "lane distance");
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    a = __builtin_bit_cast(float, (uint32_t)r[0]);
+    b = __builtin_bit_cast(float, (uint32_t)r[1]);
+  }
+}
+
+#ifdef FA8_DECODE_WAVES_PER_EU
+#define FA8_DECODE_OCCUPANCY __attribute__((amdgpu_waves_per_eu(FA8_DECODE_WAVES_PER_EU)))
+#else
+#define FA8_DECODE_OCCUPANCY
+#endif
+
+template <int D, int GWW, int HG, bool kFp8, int NW, int PD>
+__global__ __launch_bounds__(64 * NW) FA8_DECODE_OCCUPANCY void decode_split_kernel(DecodeParams p) {
+  constexpr int ES = kFp8 ? 1 : 2;                     // bytes per element
+  constexpr int CB = (kFp8 && D == 64) ? 8 : 16;       // bytes per lane chunk
+  constexpr int CW = CB / 4;                           // dwords per chunk
+  constexpr int EPC = CB / ES;                         // elements per chunk
+  constexpr int LPT = D / EPC;                         // lanes per row
+  constexpr int TPW = 64 / LPT;                        // rows per wave-load
+  constexpr int RPL = kBlockSize / TPW;                // rows per lane per page
   constexpr int ROW_BYTES = D * ES;
   constexpr int HALF_BYTES = kBlockSize * ROW_BYTES;
+  constexpr int GW = GWW * HG;                         // query heads per workgroup
+  constexpr int NPW = NW / HG;                         // waves sharing one head group
   static_assert(LPT * TPW == 64 && RPL * TPW == kBlockSize, "tiling");
+  static_assert(!kFp8 || RPL % 2 == 0, "e4m3 p.v pairs rows of a lane");
+  static_assert(NW % HG == 0 && PD >= 2 && PD <= 8, "launch shape");
+  using C = Chunk<CW>;
+  constexpr bool kF16PV = FA8_DECODE_F16_PV != 0;
 
   const int split = blockIdx.x;
   const int G = p.num_q_heads / p.num_kv_heads;
@@ -135,6 +225,8 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeParams p) {
   const int b = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hg = wave % HG;        // which GWW query heads this wave serves
+  const int pw = wave / HG;        // which pages of the split it reads
   const int slot = lane / LPT;
   const int c = lane % LPT;
 
@@ -145,12 +237,13 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeParams p) {
   const int pg0 = page_lo + split * p.pages_per_split;
   const int pg1 = min(pg0 + p.pages_per_split, page_hi);
 
-  // q slice (bf16 pairs) for d = c*EPC .. c*EPC+EPC-1 of each query head
-  uint32_t qw[GW][EPC / 2];
+  // q columns c*EPC .. c*EPC+EPC-1 of this wave's query heads, as bf16 pairs
+  const int hqw = hq0 + hg * GWW;
+  uint32_t qw[GWW][EPC / 2];
 #pragma unroll
-  for (int g = 0; g < GW; ++g) {
+  for (int g = 0; g < GWW; ++g) {
     const uint4* src = reinterpret_cast<const uint4*>(
-        p.q + ((size_t)b * p.num_q_heads + hq0 + g) * D + c * EPC);
+        p.q + ((size_t)b * p.num_q_heads + hqw + g) * D + c * EPC);
 #pragma unroll
     for (int i = 0; i < EPC / 8; ++i) {
       const uint4 w = src[i];
@@ -162,149 +255,217 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeParams p) {
   }
   const float qk_scale = p.sm_scale * kLog2e * (kFp8 ? p.k_scale[h] : 1.0f);
 
-  float m[GW], l[GW], o[GW][EPC];
+  float m[GWW], l[GWW], o[GWW][EPC];
 #pragma unroll
-  for (int g = 0; g < GW; ++g) {
+  for (int g = 0; g < GWW; ++g) {
     m[g] = kNegInf;
     l[g] = 0.f;
 #pragma unroll
     for (int e = 0; e < EPC; ++e) o[g][e] = 0.f;
   }
 
-  const uint8_t* head_base = p.cache + (size_t)h * 2 * HALF_BYTES;
+  const uint8_t* head_base = p.cache + (size_t)h * 2 * HALF_BYTES + slot * ROW_BYTES + c * CB;
   const size_t blk_stride = (size_t)p.num_kv_heads * 2 * HALF_BYTES;
   const int32_t* bt = p.block_table + (size_t)b * p.max_blocks;
-  const int lane_off = slot * ROW_BYTES + c * 16;
 
-  uint4 kr[RPL], vr[RPL];
-  auto load_page = [&](int pg, uint4(&kd)[RPL], uint4(&vd)[RPL]) {
-    const uint8_t* kb = head_base + (size_t)bt[pg] * blk_stride + lane_off;
+  struct Page {
+    C k[RPL], v[RPL];
+  };
+  auto issue = [&](Page& pg, int blk) {
+    const uint8_t* kb = head_base + (size_t)blk * blk_stride;
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) pg.k[r] = load_chunk<CW>(kb + r * TPW * ROW_BYTES);
 #pragma unroll
     for (int r = 0; r < RPL; ++r)
-      kd[r] = *reinterpret_cast<const uint4*>(kb + r * TPW * ROW_BYTES);
-#pragma unroll
-    for (int r = 0; r < RPL; ++r)
-      vd[r] = *reinterpret_cast<const uint4*>(kb + HALF_BYTES + r * TPW * ROW_BYTES);
+      pg.v[r] = load_chunk<CW>(kb + HALF_BYTES + r * TPW * ROW_BYTES);
   };
 
-  int pg = pg0 + wave;
-  if (pg < pg1) load_page(pg, kr, vr);
-  for (; pg < pg1; pg += NW) {
-    uint4 kn[RPL], vn[RPL];
-    const int pn = pg + NW;
-    if (pn < pg1) load_page(pn, kn, vn);
-
-    // ---- scores s = (q . k) * sm_scale * k_scale * log2(e) ----------------
-    float s[RPL][GW];
+  // One page, straight-line: the pages at the window start and sequence end
+  // differ only in the validity mask (a select), so there is a single path.
+  auto run_page = [&](const Page& pg, int page) {
+    // ---- scores s = (q . k) * sm_scale * k_scale * log2(e) ------------------
+    float s[RPL][GWW];
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
-      const int tok = pg * kBlockSize + slot + r * TPW;
-      const bool valid = tok >= lo && tok < L;
-      const uint32_t kw[4] = {kr[r].x, kr[r].y, kr[r].z, kr[r].w};
-      float part[GW];
+      float part[GWW];
 #pragma unroll
-      for (int g = 0; g < GW; ++g) part[g] = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < CW; ++w) {
         if constexpr (kFp8) {
-          const bf16x2 k01 = e4m3x2_to_bf16<false>(kw[w]);
-          const bf16x2 k23 = e4m3x2_to_bf16<true>(kw[w]);
+          const bf16x2 k01 = e4m3x2_to_bf16<false>(pg.k[r].w[w]);
+          const bf16x2 k23 = e4m3x2_to_bf16<true>(pg.k[r].w[w]);
 #pragma unroll
-          for (int g = 0; g < GW; ++g) {
-            part[g] = dot2_bf16(as_bf16x2(qw[g][2 * w]), k01, part[g]);
+          for (int g = 0; g < GWW; ++g) {
+            part[g] = dot2_bf16(as_bf16x2(qw[g][2 * w]), k01, w == 0 ? 0.f : part[g]);
             part[g] = dot2_bf16(as_bf16x2(qw[g][2 * w + 1]), k23, part[g]);
           }
         } else {
 #pragma unroll
-          for (int g = 0; g < GW; ++g)
-            part[g] = dot2_bf16(as_bf16x2(qw[g][w]), as_bf16x2(kw[w]), part[g]);
+          for (int g = 0; g < GWW; ++g)
+            part[g] = dot2_bf16(as_bf16x2(qw[g][w]), as_bf16x2(pg.k[r].w[w]),
+                                w == 0 ? 0.f : part[g]);
         }
       }
 #pragma unroll
-      for (int g = 0; g < GW; ++g) {
-        const float full = group_sum<LPT>(part[g]);
-        s[r][g] = valid ? full * qk_scale : kNegInf;
+      for (int g = 0; g < GWW; ++g) s[r][g] = group_sum<LPT>(part[g]) * qk_scale;
+    }
+    // only the pages at the window start / sequence end hold invisible rows
+    if (page * kBlockSize < lo || page * kBlockSize + kBlockSize > L) {
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) {
+        const int tok = page * kBlockSize + slot + r * TPW;
+        const bool valid = tok >= lo && tok < L;
+#pragma unroll
+        for (int g = 0; g < GWW; ++g) s[r][g] = valid ? s[r][g] : kNegInf;
       }
     }
-
-    // ---- online softmax: raise the running max, rescale when it moves ----
+    // ---- reference maximum ---------------------------------------------------
+    // m is the slot's reference point, not necessarily its exact maximum: it
+    // moves (and the state is rescaled) only when a score exceeds it by more
+    // than kLazy (log2 units), so p = 2^(s - m) stays below 2^kLazy and the
+    // rescale is rare.  The result is the same softmax (any reference works).
+    float mref[GWW];
 #pragma unroll
-    for (int g = 0; g < GW; ++g) {
+    for (int g = 0; g < GWW; ++g) {
       float mx = s[0][g];
 #pragma unroll
       for (int r = 1; r < RPL; ++r) mx = fmaxf(mx, s[r][g]);
-      if (mx > m[g]) {
-        const float alpha = fast_exp2(m[g] - mx);  // 0 when m was -inf
+      if (mx > m[g] + kLazy) {
+        const float alpha = fast_exp2(m[g] - mx);  // 0 while m is -inf
         l[g] *= alpha;
 #pragma unroll
         for (int e = 0; e < EPC; ++e) o[g][e] *= alpha;
         m[g] = mx;
       }
+      // while nothing is visible yet (m = -inf) every s is -inf: use 0 as the
+      // reference so that exp2(s - ref) = 0 instead of NaN
+      mref[g] = m[g] > kNegInf ? m[g] : 0.f;
     }
-
-    // ---- P.V in fp32 -------------------------------------------------------
+    // ---- probabilities ---------------------------------------------------------
+    float pr[RPL][GWW];
 #pragma unroll
-    for (int r = 0; r < RPL; ++r) {
-      float vf[EPC];
-      const uint32_t vw[4] = {vr[r].x, vr[r].y, vr[r].z, vr[r].w};
+    for (int r = 0; r < RPL; ++r)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        if constexpr (kFp8) {
-          const f32x2 a = e4m3x2_to_f32<false>(vw[w]);
-          const f32x2 bb = e4m3x2_to_f32<true>(vw[w]);
-          vf[4 * w + 0] = a.x;
-          vf[4 * w + 1] = a.y;
-          vf[4 * w + 2] = bb.x;
-          vf[4 * w + 3] = bb.y;
-        } else {
-          vf[2 * w + 0] = bf16_lo(vw[w]);
-          vf[2 * w + 1] = bf16_hi(vw[w]);
+      for (int g = 0; g < GWW; ++g) {
+        pr[r][g] = fast_exp2(s[r][g] - mref[g]);
+        l[g] += pr[r][g];
+      }
+    // ---- p . v -------------------------------------------------------------
+    if constexpr (kFp8 && kF16PV) {
+#pragma unroll
+      for (int r = 0; r < RPL; r += 2) {
+        f16x2 vp[EPC];
+#pragma unroll
+        for (int w = 0; w < CW; ++w) {
+          // bytes [a0 b0 a1 b1] and [a2 b2 a3 b3] of rows r (a) and r+1 (b)
+          const uint32_t lo2 = __builtin_amdgcn_perm(pg.v[r + 1].w[w], pg.v[r].w[w], 0x05010400u);
+          const uint32_t hi2 = __builtin_amdgcn_perm(pg.v[r + 1].w[w], pg.v[r].w[w], 0x07030602u);
+          vp[4 * w + 0] = e4m3x2_to_f16<false>(lo2);
+          vp[4 * w + 1] = e4m3x2_to_f16<true>(lo2);
+          vp[4 * w + 2] = e4m3x2_to_f16<false>(hi2);
+          vp[4 * w + 3] = e4m3x2_to_f16<true>(hi2);
+        }
+#pragma unroll
+        for (int g = 0; g < GWW; ++g) {
+          const f16x2 pp = {(_Float16)pr[r][g], (_Float16)pr[r + 1][g]};
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) o[g][e] = dot2_f16(vp[e], pp, o[g][e]);
         }
       }
+    } else {
 #pragma unroll
-      for (int g = 0; g < GW; ++g) {
-        const float pr = s[r][g] > kNegInf ? fast_exp2(s[r][g] - m[g]) : 0.f;
-        l[g] += pr;
+      for (int r = 0; r < RPL; ++r) {
+        float vf[EPC];
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) o[g][e] = fmaf(pr, vf[e], o[g][e]);
+        for (int w = 0; w < CW; ++w) {
+          if constexpr (kFp8) {
+            const f32x2 x01 = e4m3x2_to_f32<false>(pg.v[r].w[w]);
+            const f32x2 x23 = e4m3x2_to_f32<true>(pg.v[r].w[w]);
+            vf[4 * w + 0] = x01.x;
+            vf[4 * w + 1] = x01.y;
+            vf[4 * w + 2] = x23.x;
+            vf[4 * w + 3] = x23.y;
+          } else {
+            vf[2 * w + 0] = bf16_lo(pg.v[r].w[w]);
+            vf[2 * w + 1] = bf16_hi(pg.v[r].w[w]);
+          }
+        }
+#pragma unroll
+        for (int g = 0; g < GWW; ++g)
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) o[g][e] = fmaf(pr[r][g], vf[e], o[g][e]);
       }
     }
+  };
 
+  // This wave's pages: pg0 + pw + NPW*j.  Block ids are fetched 64 at a
+  // time, one per lane, and broadcast with readlane; PD-1 pages are in
+  // flight while one is processed.
+  const int first = pg0 + pw;
+  const int npw = first < pg1 ? (pg1 - first + NPW - 1) / NPW : 0;
+  for (int jb = 0; jb < npw; jb += 64) {
+    const int n = min(64, npw - jb);
+    const int page_base = first + NPW * jb;
+    const int my_blk = lane < n ? bt[page_base + NPW * lane] : 0;
+    // Steady PD-deep ring: PD-1 pages are in flight while one is processed.
+    // Every buffer is consumed and re-issued in every round, and prefetches
+    // past the end repeat the last page (an L2 hit), so every path keeps the
+    // same loads in flight and the compiler waits for exactly the page it is
+    // about to use.
+    auto blk_of = [&](int j) { return __builtin_amdgcn_readlane(my_blk, min(j, n - 1)); };
+    Page ring[PD];
 #pragma unroll
-    for (int r = 0; r < RPL; ++r) {
-      kr[r] = kn[r];
-      vr[r] = vn[r];
+    for (int k = 0; k < PD; ++k) issue(ring[k], blk_of(k));
+    int j = 0;
+    for (; j + PD <= n; j += PD) {
+#pragma unroll
+      for (int k = 0; k < PD; ++k) {
+        run_page(ring[k], page_base + NPW * (j + k));
+        __builtin_amdgcn_sched_barrier(0);   // keep the reissue after the use
+        issue(ring[k], blk_of(j + k + PD));
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
+#pragma unroll
+    for (int k = 0; k < PD - 1; ++k)
+      if (j + k < n) run_page(ring[k], page_base + NPW * (j + k));
   }
 
   // ---- merge the TPW row slots of the wave (lanes with equal c) -------------
+  // Slots sit LPT, 2*LPT, ... lanes apart; each step merges a lane's state
+  // with its partner's (a symmetric merge, so both partners end up equal).
+  auto merge_step = [&](auto xtag) {
+    constexpr int X = decltype(xtag)::value;
 #pragma unroll
-  for (int x = LPT; x < 64; x *= 2) {
-#pragma unroll
-    for (int g = 0; g < GW; ++g) {
-      const float om = __shfl_xor(m[g], x);
-      const float ol = __shfl_xor(l[g], x);
-      const float M = fmaxf(m[g], om);
-      const float a = m[g] > kNegInf ? fast_exp2(m[g] - M) : 0.f;
-      const float bw = om > kNegInf ? fast_exp2(om - M) : 0.f;
-      l[g] = a * l[g] + bw * ol;
+    for (int g = 0; g < GWW; ++g) {
+      float ma, mb, la, lb;
+      lane_pair<X>(m[g], ma, mb);
+      lane_pair<X>(l[g], la, lb);
+      const float M = fmaxf(ma, mb);
+      const float fa = ma > kNegInf ? fast_exp2(ma - M) : 0.f;
+      const float fb = mb > kNegInf ? fast_exp2(mb - M) : 0.f;
+      l[g] = fa * la + fb * lb;
 #pragma unroll
       for (int e = 0; e < EPC; ++e) {
-        const float oo = __shfl_xor(o[g][e], x);
-        o[g][e] = a * o[g][e] + bw * oo;
+        float oa, ob;
+        lane_pair<X>(o[g][e], oa, ob);
+        o[g][e] = fa * oa + fb * ob;
       }
       m[g] = M;
     }
-  }
+  };
+  if constexpr (LPT <= 8) merge_step(std::integral_constant<int, 8>{});
+  if constexpr (LPT <= 16) merge_step(std::integral_constant<int, 16>{});
+  if constexpr (LPT <= 32) merge_step(std::integral_constant<int, 32>{});
 
-  // ---- merge the NW waves through LDS and write the split's partial --------
-  __shared__ float s_o[NW][GW][D];
-  __shared__ float s_m[NW][GW];
-  __shared__ float s_l[NW][GW];
+  // ---- merge the waves of each head group through LDS (one round) ----------
+  __shared__ float s_o[NW][GWW][D];
+  __shared__ float s_m[NW][GWW];
+  __shared__ float s_l[NW][GWW];
   __shared__ int s_last;
+  const int S = p.num_splits;
   if (slot == 0) {
 #pragma unroll
-    for (int g = 0; g < GW; ++g) {
+    for (int g = 0; g < GWW; ++g) {
 #pragma unroll
       for (int e = 0; e < EPC; ++e) s_o[wave][g][c * EPC + e] = o[g][e];
       if (c == 0) {
@@ -314,42 +475,44 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeParams p) {
     }
   }
   __syncthreads();
-  const int S = p.num_splits;
-  for (int idx = threadIdx.x; idx < GW * D; idx += 64 * NW) {
-    const int g = idx / D;
-    const int d = idx % D;
+  // element t: head group hgi, local head g, column d; all stores are issued
+  // back to back and waited for once below
+  for (int t = threadIdx.x; t < HG * GWW * D; t += 64 * NW) {
+    const int hgi = t / (GWW * D);
+    const int g = (t / D) % GWW;
+    const int d = t % D;
     float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][g]);
+    for (int w = hgi; w < NW; w += HG) M = fmaxf(M, s_m[w][g]);
     float num = 0.f, den = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float mw = s_m[w][g];
-      const float f = mw > kNegInf ? fast_exp2(mw - M) : 0.f;
+    for (int w = hgi; w < NW; w += HG) {
+      const float f = s_m[w][g] > kNegInf ? fast_exp2(s_m[w][g] - M) : 0.f;
       num += f * s_o[w][g][d];
       den += f * s_l[w][g];
     }
-    const size_t row = ((size_t)b * p.num_q_heads + hq0 + g) * S + split;
-    p.ws_o[row * D + d] = num;
+    const size_t row = ((size_t)b * p.num_q_heads + hq0 + hgi * GWW + g) * S + split;
+    st_agent(p.ws_o + row * D + d, num);
     if (d == 0) {
-      p.ws_m[row] = M;
-      p.ws_l[row] = den;
+      st_agent(p.ws_m + row, M);
+      st_agent(p.ws_l + row, den);
     }
   }
 
   // ---- the last workgroup of this (sequence, head group) merges the splits -
-  // Release the partials device-wide and count arrivals; the workgroup that
-  // arrives last acquires them, writes the output and re-arms the counter so
-  // the workspace is ready for the next call.  No workgroup ever waits.
-  __threadfence();
+  // Each thread waits until its partial stores are performed (they are
+  // coherent agent-scope stores), the workgroup then counts its arrival; the
+  // one that arrives last reads the partials with coherent loads, writes the
+  // output and re-arms the counter for the next call.  No workgroup waits.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   int* counter = p.ws_count + (size_t)b * gridDim.y + blockIdx.y;
-  if (threadIdx.x == 0) s_last = (atomicAdd(counter, 1) == S - 1);
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
   combine_splits<D, GW, NW>(p, b, h, hq0);
-  if (threadIdx.x == 0) *counter = 0;
+  if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 static size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
@@ -377,18 +540,40 @@ void decode_workspace_carve(void* ws, int batch, int num_q_heads, int head_dim, 
   *l = reinterpret_cast<float*>(base + align16(rows * head_dim * 4) + align16(rows * 4));
 }
 
+#ifndef FA8_DECODE_PIPE
+#define FA8_DECODE_PIPE 2      // e4m3 cache: pages held per wave (in flight + processed)
+#endif
+#ifndef FA8_DECODE_PIPE_BF16
+#define FA8_DECODE_PIPE_BF16 2 // bf16 cache (pages are twice as large)
+#endif
+#ifndef FA8_DECODE_MAX_GWW
+#define FA8_DECODE_MAX_GWW 4   // query heads per wave for head_dim 64 / 128
+#endif
+
+// Launch shape per (D, cache type): query heads per wave (GWW), waves per
+// workgroup (NW).  Heads of one KV head beyond GWW go to other waves of the
+// same workgroup (head groups), which read the same pages (L2 hits).
+template <int D, bool kFp8, int GWW, int HG>
+static void launch_shape(const DecodeParams& p, dim3 grid, hipStream_t stream) {
+  constexpr int NW = kDecodeWaves;
+  constexpr int PD = kFp8 ? FA8_DECODE_PIPE : FA8_DECODE_PIPE_BF16;
+  hipLaunchKernelGGL((decode_split_kernel<D, GWW, HG, kFp8, NW, PD>), grid,
+                     dim3(64 * NW), 0, stream, p);
+}
+
 template <int D, bool kFp8>
 static hipError_t launch_decode_d(const DecodeParams& p, hipStream_t stream) {
-  constexpr int NW = 4;
+  // at most 4 query heads per wave (2 for head_dim 256) keeps registers
+  // below the spill point; at most 8 heads per workgroup
+  constexpr int kMaxGWW = D == 256 ? 2 : FA8_DECODE_MAX_GWW;
   const int G = p.num_q_heads / p.num_kv_heads;
   const int GW = G > 8 ? 8 : G;
   dim3 grid(p.num_splits, p.num_kv_heads * (G / GW), p.batch);
-  dim3 block(64 * NW);
   switch (GW) {
-    case 1: hipLaunchKernelGGL((decode_split_kernel<D, 1, kFp8, NW>), grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2, kFp8, NW>), grid, block, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((decode_split_kernel<D, 4, kFp8, NW>), grid, block, 0, stream, p); break;
-    case 8: hipLaunchKernelGGL((decode_split_kernel<D, 8, kFp8, NW>), grid, block, 0, stream, p); break;
+    case 1: launch_shape<D, kFp8, 1, 1>(p, grid, stream); break;
+    case 2: launch_shape<D, kFp8, 2, 1>(p, grid, stream); break;
+    case 4: launch_shape<D, kFp8, (4 > kMaxGWW ? kMaxGWW : 4), (4 > kMaxGWW ? 4 / kMaxGWW : 1)>(p, grid, stream); break;
+    case 8: launch_shape<D, kFp8, kMaxGWW, 8 / kMaxGWW>(p, grid, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

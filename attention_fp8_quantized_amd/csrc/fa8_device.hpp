@@ -65,6 +65,17 @@ __device__ __forceinline__ bf16x2 e4m3x2_to_bf16(uint32_t w) {
   return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHi);
 }
 
+// Two e4m3 codes -> packed f16 pair (exact: f16 holds every e4m3 value).
+template <bool kHi>
+__device__ __forceinline__ f16x2 e4m3x2_to_f16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, kHi);
+}
+
+// acc + a.x*b.x + a.y*b.y  (products of f16 are exact in fp32)
+__device__ __forceinline__ float dot2_f16(f16x2 a, f16x2 b, float acc) {
+  return __builtin_amdgcn_fdot2(a, b, acc, false);
+}
+
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) {
   return __builtin_bit_cast(bf16x2, w);
 }

@@ -35,7 +35,11 @@ struct DecodeParams {
 // int32 arrival counters [B][Hq] (zero before the first call; every call
 // leaves them zero), then fp32 o_part [B][Hq][S][D], m [B][Hq][S] and
 // l [B][Hq][S].
-constexpr int kDecodeMaxSplits = 1024;
+constexpr int kDecodeMaxSplits = 256;
+#ifndef FA8_DECODE_WAVES
+#define FA8_DECODE_WAVES 8
+#endif
+constexpr int kDecodeWaves = FA8_DECODE_WAVES;   // waves per decode workgroup
 size_t decode_workspace_bytes(int batch, int num_q_heads, int head_dim, int splits);
 void decode_workspace_carve(void* ws, int batch, int num_q_heads, int head_dim, int splits,
                             int** count, float** o, float** m, float** l);

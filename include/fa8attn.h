@@ -117,7 +117,7 @@ size_t fa8_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
  *   sm_scale     softmax scale (usually 1/sqrt(head_dim)).
  *   window       > 0: attend to the last `window` keys (the query's own
  *                token included); <= 0: the whole context.
- *   num_splits   context splits, 0..1024; 0 = fa8_decode_num_splits(...).
+ *   num_splits   context splits, 0..256; 0 = fa8_decode_num_splits(...).
  *   out          fp32 [batch][num_q_heads][head_dim]
  *                out = sum_j softmax(sm_scale * q.K_j) * V_j.
  *   workspace    >= fa8_decode_workspace_bytes(batch, num_q_heads,

@@ -76,6 +76,12 @@ class DecodeCase:
         else:
             self.ks = self.vs = np.ones(Hkv, dtype=np.float32)
         self.slots = W.all_slots(self.bt, self.lens)
+        # host-side bounds checks before anything is launched
+        need = W.blocks_needed(self.lens)
+        for b, n in enumerate(need):
+            assert np.all((self.bt[b, :n] >= 0) & (self.bt[b, :n] < max(self.nblocks, 1)))
+        assert self.bt.shape[1] * 16 >= (int(self.lens.max()) if B else 0)
+        assert len(self.slots) == N and (N == 0 or self.slots.max() < self.nblocks * 16)
         qb, self.q = W.bf16_values(np.zeros((B, Hq, D), np.float32) if q_zero
                                    else W.normal(W.rng(seed, 0, W.Q), (B, Hq, D)))
         self.k, self.v = k, v

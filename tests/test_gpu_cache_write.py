@@ -22,12 +22,24 @@ pytestmark = pytest.mark.gpu
 def _gpu_write(k, v, slots, ks, vs, nblocks, Hkv, D, cd, in_bf16=False, fill=None):
     import torch
     import attention_fp8_quantized_amd as fa
+    slots = np.asarray(slots, np.int64)
+    # host-side bounds check before anything is launched
+    assert slots.max() < nblocks * 16 and len(np.unique(slots[slots >= 0])) == (slots >= 0).sum()
+    assert k.shape == v.shape == (len(slots), Hkv, D)
     cache = fa.new_cache(nblocks, Hkv, D, cd)
     if fill is not None:
         cache.view(torch.uint8).fill_(fill)
     kt, vt = dev(k), dev(v)
     if in_bf16:
-        kt, vt = kt.to(torch.bfloat16), vt.to(torch.bfloat16)
+        def to_bf16(a):
+            bits = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+            if np.all((bits & 0xFFFF) == 0):
+                # exact bf16 patterns: keep every bit (torch's cast would
+                # replace NaN payloads and signs by its canonical NaN)
+                hi = (bits >> 16).astype(np.uint16).view(np.int16)
+                return torch.from_numpy(hi).cuda().view(torch.bfloat16)
+            return dev(a).to(torch.bfloat16)
+        kt, vt = to_bf16(k), to_bf16(v)
     fa.cache_write(kt, vt, dev(np.asarray(slots, np.int64)), dev(ks), dev(vs), cache)
     torch.cuda.synchronize()
     out = cache.cpu()
@@ -88,7 +100,7 @@ def test_random_and_edges(D):
     ks = g.uniform(0.001, 3.0, Hkv).astype(np.float32)
     vs = g.uniform(0.001, 3.0, Hkv).astype(np.float32)
     slots = g.permutation(N * 2)[:N]
-    nb = N * 2 // 16
+    nb = (N * 2 + 15) // 16
     log(f"cache_write random+edges D={D}")
     want = _oracle_write(k, v, slots, ks, vs, nb, Hkv, D, "e4m3", fill=0xA5)
     got = _gpu_write(k, v, slots, ks, vs, nb, Hkv, D, "e4m3", fill=0xA5)

@@ -58,17 +58,23 @@ def test_sliding_window(window, cd):
     _check(c, f"window={window} {cd}")
 
 
-def test_split_count_invariance():
-    c = DecodeCase(2, 32, 8, 128, [5000, 3333], "e4m3", seed=30)
+@pytest.mark.parametrize("cd", ["e4m3", "bf16"])
+def test_split_count_invariance(cd):
+    # Splits only regroup the same sums.  The bf16 cache path is fp32 all the
+    # way (agreement to fp32 rounding); the e4m3 path rounds each probability
+    # to f16 relative to its row slot's running maximum, so its rounding
+    # pattern (and a ~1e-4 relative error) depends on how tokens are grouped.
+    c = DecodeCase(2, 32, 8, 128, [5000, 3333], cd, seed=30)
     ref, qheads = c.oracle()
     outs = {}
-    for s in [1, 2, 3, 7, 0, 64, 313]:
+    for s in [1, 2, 3, 7, 0, 64, 250]:
         log(f"decode splits={s}")
         outs[s] = c.run_gpu(num_splits=s)
         assert_gate(outs[s][:, qheads], ref, f"splits={s}")
+    tol = 2e-6 if cd == "bf16" else 6e-4
     for s, o in outs.items():
         ma, rl = metrics(o, outs[1])
-        assert rl < 2e-6, (s, rl)
+        assert rl < tol, (s, rl)
 
 
 def test_page_permutation_invariance():
