@@ -163,8 +163,16 @@ def quantize_query(q, q_scale):
     return np.float64(np.float32(q_scale)) * decode(codes)
 
 
+def _prefill_rows_pair(q, cu_q_lens, cache, block_table, seq_lens, q_scale, k_scale,
+                       v_scale, sm_scale, window, rows, row_fn):
+    """Like _prefill_rows for a row function returning a [2][D] array."""
+    out = _prefill_rows(q, cu_q_lens, cache, block_table, seq_lens, q_scale, k_scale,
+                        v_scale, sm_scale, window, rows, row_fn, width=2)
+    return out[:, :, 0, :].copy(), out[:, :, 1, :].copy()
+
+
 def _prefill_rows(q, cu_q_lens, cache, block_table, seq_lens, q_scale, k_scale,
-                  v_scale, sm_scale, window, rows, row_fn):
+                  v_scale, sm_scale, window, rows, row_fn, width=None):
     q = np.asarray(q, dtype=np.float64)
     Ttot, Hq, D = q.shape
     Hkv = cache.shape[1]
@@ -175,7 +183,8 @@ def _prefill_rows(q, cu_q_lens, cache, block_table, seq_lens, q_scale, k_scale,
         rows = np.arange(Ttot)
     rows = np.asarray(rows, dtype=np.int64)
     qhat = quantize_query(q[rows], q_scale)            # [R][Hq][D]
-    out = np.zeros((len(rows), Hq, D), dtype=np.float64)
+    shape = (len(rows), Hq, D) if width is None else (len(rows), Hq, width, D)
+    out = np.zeros(shape, dtype=np.float64)
     seq_of = np.searchsorted(cu, rows, side="right") - 1
     for b in np.unique(seq_of):
         sel = np.nonzero(seq_of == b)[0]
@@ -214,7 +223,7 @@ def prefill_exact(q, cu_q_lens, cache, block_table, seq_lens, q_scale, k_scale,
                          k_scale, v_scale, sm_scale, window, rows, _exact_row)
 
 
-def mirror_row(s, keys, V, kv_tile, quantize_p=True):
+def mirror_row(s, keys, V, kv_tile, quantize_p=True, flip_tol=0.0, return_slack=False):
     """One query row of the tile-mirrored reference, closed form.
 
     s     scores (float64) of the visible keys, in ascending key order
@@ -237,11 +246,26 @@ def mirror_row(s, keys, V, kv_tile, quantize_p=True):
     pq = decode(encode(p)) if quantize_p else p
     w_tile = np.exp(m_j - m_run[-1])
     l = (p * w_tile).sum()
-    return ((pq * w_tile) @ V) / l
+    o = ((pq * w_tile) @ V) / l
+    if not return_slack:
+        return o
+    # Flip allowance: a kernel computes p in float32, so a p that lies within
+    # a relative flip_tol of an e4m3 rounding midpoint may legitimately round
+    # to the neighbouring code.  slack bounds, per output element, how far
+    # such alternative roundings can move o.
+    slack = np.zeros(V.shape[1])
+    if quantize_p and flip_tol > 0:
+        alt_lo = decode(encode(p * (1.0 - flip_tol)))
+        alt_hi = decode(encode(p * (1.0 + flip_tol)))
+        dq = np.maximum(np.abs(alt_lo - pq), np.abs(alt_hi - pq))
+        if np.any(dq > 0):
+            slack = ((dq * w_tile) @ np.abs(V)) / l
+    return o, slack
 
 
 def prefill_mirror(q, cu_q_lens, cache, block_table, seq_lens, q_scale, k_scale,
-                   v_scale, sm_scale, window, kv_tile, rows=None, quantize_p=True):
+                   v_scale, sm_scale, window, kv_tile, rows=None, quantize_p=True,
+                   flip_tol=None):
     """Tile-mirrored FP8-P reference (the parity target of the prefill kernel).
 
     ``kv_tile`` is the key-tile width the kernel visits (its value is part of
@@ -253,9 +277,17 @@ def prefill_mirror(q, cu_q_lens, cache, block_table, seq_lens, q_scale, k_scale,
     closed form (p = 1 quantises exactly, o = mean V), by kv_tile >= n reducing
     to quantising exp(s - max s), and by a hand-written tiny example.
     """
-    fn = lambda s, keys, V: mirror_row(s, keys, V, kv_tile, quantize_p)  # noqa: E731
-    return _prefill_rows(q, cu_q_lens, cache, block_table, seq_lens, q_scale,
-                         k_scale, v_scale, sm_scale, window, rows, fn)
+    if flip_tol is None:
+        fn = lambda s, keys, V: mirror_row(s, keys, V, kv_tile, quantize_p)  # noqa: E731
+        return _prefill_rows(q, cu_q_lens, cache, block_table, seq_lens, q_scale,
+                             k_scale, v_scale, sm_scale, window, rows, fn)
+    # With flip_tol: returns (out, slack), slack stacked after out along a
+    # new leading axis of length 2 in the per-row function, split here.
+    fn = lambda s, keys, V: np.stack(mirror_row(s, keys, V, kv_tile, quantize_p,  # noqa: E731
+                                                flip_tol, True))
+    both = _prefill_rows_pair(q, cu_q_lens, cache, block_table, seq_lens, q_scale,
+                              k_scale, v_scale, sm_scale, window, rows, fn)
+    return both[0], both[1]
 
 
 def recurrence_row(s, keys, V, kv_tile, quantize_p=True):

@@ -380,3 +380,32 @@ def test_prefill_literal_tiny():
                 l = a * l + ls
                 m = mn
             np.testing.assert_allclose(got[i, hq], [O[d] / l for d in range(4)], rtol=1e-12)
+
+
+def test_flip_slack_covers_perturbed_scores():
+    # scores perturbed by a relative 1e-7 (float32-sized error) may flip e4m3
+    # roundings of p; the slack must bound the change of every output element
+    g = np.random.default_rng(21)
+    kv_tile = 16
+    worst = 0.0
+    for trial in range(200):
+        n = int(g.integers(1, 60))
+        keys = np.arange(n)
+        s = g.standard_normal(n) * 2
+        V = g.standard_normal((n, 4))
+        o, slack = A.mirror_row(s, keys, V, kv_tile, True, 4e-6, True)
+        for k in range(5):
+            sp = s * (1 + g.uniform(-1e-7, 1e-7, n))
+            op = A.mirror_row(sp, keys, V, kv_tile, True)
+            excess = np.abs(op - o) - slack
+            worst = max(worst, excess.max())
+    # only float64 rounding noise (and the unquantised denominator's own
+    # change, ~1e-7 relative) may remain
+    assert worst < 1e-6, worst
+
+
+def test_flip_slack_zero_without_midpoints():
+    # p = 1 exactly and p = 0.5 exactly are codes, far from any midpoint
+    s = np.array([0.0, np.log(0.5)])
+    o, slack = A.mirror_row(s, np.arange(2), np.eye(2), 16, True, 4e-6, True)
+    assert np.all(slack == 0)
