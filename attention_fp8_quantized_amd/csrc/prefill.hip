@@ -1,11 +1,302 @@
-// FP8 prefill (placeholder until the MFMA kernel lands).
+// Causal FP8 prefill over the paged cache with two-level accumulation.
+//
+// [BLOG] "Introduction": both matmuls of attention, QK and Score*V, run in
+// e4m3.  "Kernel and vLLM improvements / Two-level accumulation": the P*V
+// partial sums of a tile are flushed into true fp32 registers, so the error
+// does not grow with the contraction length (the context).  "Query
+// Quantization Fusion": the query is quantised with a per-tensor scale right
+// before attention -- here in the kernel's prologue.
+//
+// Work decomposition: one workgroup of 4 waves per (64 query rows, query
+// head, sequence); each wave owns 16 query rows.  Keys are visited in tiles
+// of 128 at absolute, 128-aligned positions, in ascending order (this order
+// and width are part of the numeric contract, see fa8_prefill_kv_tile).
+//
+// Per KV tile:
+//   * the tile's K and V rows (8 pages) are copied into LDS with 16-byte
+//     loads; K codes are widened to bf16 on the way (exact: bf16 holds every
+//     e4m3 value), V stays e4m3;
+//   * S^T = K . Q^T on v_mfma_f32_16x16x32_bf16: the A operand is 8 K values
+//     of one key row per lane, the B operand the e4m3-quantised query
+//     (decoded to bf16, exact; held in registers for the whole kernel).  The
+//     products are exactly the e4m3 x e4m3 products; the bf16 MFMA sums
+//     them in fp32.  (The FP8 MFMA of this chip sums its 128 products with
+//     about 13 bits below the largest one; the scores decide how each p
+//     rounds to e4m3, so they are formed with fp32 sums.)  The result leaves
+//     each lane with one query and 32 keys of the tile -- exactly the layout
+//     the P operand of P.V needs;
+//   * scores are scaled by q_scale*k_scale*sm_scale*log2(e), masked (causal,
+//     window), the running row maximum m_t is updated, p = 2^(s - m_t) in
+//     fp32; l = alpha*l + sum p (fp32, unquantised);
+//   * P is rounded to e4m3 (round-to-nearest-even, the hardware packed
+//     convert; unit scale, p in [0, 1]);
+//   * V^T operand: ds_read_b64_tr_b8 gathers, for 16 lanes, one byte column
+//     of 8 key rows; the key order matches the P operand slot by slot;
+//   * P~ . V~ on the FP8 MFMA v_mfma_f32_16x16x128_f8f6f4 (K = the tile's
+//     128 keys).  Level 1: acc = P~ . V~ into a zeroed fp32 accumulator;
+//     level 2: O = alpha*O + acc in VALU fp32 (every tile).  accum_mode = 0
+//     instead lets the MFMA accumulate into alpha*O.
+// Epilogue: out = O * v_scale / l.
+
 #include "fa8_device.hpp"
 #include "fa8_internal.hpp"
 
 namespace fa8 {
 
-int prefill_kv_tile(int head_dim) { return head_dim == 256 ? 64 : 64; }
+constexpr int kTileN = 128;      // keys per KV tile
+constexpr int kWaveRows = 16;    // query rows per wave
+constexpr int kWaves = 4;        // waves per workgroup
+constexpr int kBlockM = kWaveRows * kWaves;
+constexpr float kNegInfP = -__builtin_huge_valf();
 
-hipError_t launch_prefill(const PrefillParams&, hipStream_t) { return hipErrorNotSupported; }
+int prefill_kv_tile(int) { return kTileN; }
+
+__device__ __forceinline__ f32x4 mfma_fp8(i32x8 a, i32x8 b, f32x4 c) {
+  // e4m3 x e4m3 (cbsz = blgp = 0), unit block scales (E8M0 127 = 2^0)
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2* lds_i32x2_ptr;
+
+// 8 bytes per lane, transposed within each 16-lane group: lanes 2j and 2j+1
+// give the addresses of the two 8-byte halves of row j (j = 0..7); lane i of
+// the group receives byte column i of those 8 rows.
+__device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t* lds_addr) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_ptr)(lds_addr));
+}
+
+// Lanes n, n+16, n+32, n+48 hold the same query: combine across them.
+__device__ __forceinline__ float group4_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v),
+                                            __builtin_bit_cast(uint32_t, v), false, false);
+  v = fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+  r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v),
+                                       __builtin_bit_cast(uint32_t, v), false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float group4_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v),
+                                            __builtin_bit_cast(uint32_t, v), false, false);
+  v = __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+  r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v),
+                                       __builtin_bit_cast(uint32_t, v), false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
+  constexpr int KQ = D / 32;               // 32-wide chunks of the head dim (bf16 MFMA K)
+  constexpr int RSK = 2 * D + 16;          // LDS row stride of bf16 K (bytes)
+  constexpr int RSV = D + 16;              // LDS row stride of e4m3 V (bytes)
+  constexpr int DB = D / 16;               // 16-wide output column blocks
+  __shared__ __attribute__((aligned(16))) uint8_t s_kv[kTileN * (RSK + RSV)];
+  uint8_t* s_k = s_kv;
+  uint8_t* s_v = s_kv + kTileN * RSK;
+
+  const int hq = blockIdx.y;
+  const int b = blockIdx.z;
+  const int G = p.num_q_heads / p.num_kv_heads;
+  const int h = hq / G;
+  const int qs = p.cu_q_lens[b];
+  const int T = p.cu_q_lens[b + 1] - qs;
+  const int q0 = blockIdx.x * kBlockM;
+  if (q0 >= T) return;
+  const int L = p.seq_lens[b];
+  const int P0 = L - T;                    // position of the chunk's first query
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4;                 // lane group (k-slot group of the MFMA)
+  const int n = lane & 15;                 // query (S^T, P) or column (V, O) of the lane
+  const int row = q0 + wave * kWaveRows + n;   // this lane's query row (S^T layout)
+  const bool row_ok = row < T;
+  const int pos = P0 + row;
+
+  // ---- prologue: quantise this lane's slice of Q (B operand of S^T) ------
+  // q8 = e4m3(fl32(q / q_scale)); the operand holds decode(q8) as bf16
+  // (exact); q_scale enters the score multiplier.  Lane (g, n) holds query n,
+  // columns 32*kq + 8*g .. +7 for every chunk kq.
+  const float qsc = p.q_scale[0];
+  bf16x8 qb[KQ];
+#pragma unroll
+  for (int kq = 0; kq < KQ; ++kq) {
+    uint4 w4 = make_uint4(0, 0, 0, 0);
+    if (row_ok)
+      w4 = *reinterpret_cast<const uint4*>(
+          p.q + ((size_t)(qs + row) * p.num_q_heads + hq) * D + kq * 32 + g * 8);
+    const uint32_t ws[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+    for (int h2 = 0; h2 < 4; ++h2) {
+      const uint32_t c2 = e4m3_encode(bf16_lo(ws[h2]) / qsc) |
+                          (e4m3_encode(bf16_hi(ws[h2]) / qsc) << 8);
+      const bf16x2 d2 = e4m3x2_to_bf16<false>(c2);
+      qb[kq][2 * h2] = d2[0];
+      qb[kq][2 * h2 + 1] = d2[1];
+    }
+  }
+  // log2-domain score multiplier
+  const float qk = qsc * p.k_scale[h] * p.sm_scale * kLog2e;
+
+  // ---- key range of this workgroup ---------------------------------------
+  const int rmax = min(q0 + kBlockM, T) - 1;
+  const int lo_key = p.window > 0 ? max(0, P0 + q0 - p.window + 1) : 0;
+  const int hi_key = P0 + rmax;
+  const int t_lo = lo_key / kTileN;
+  const int t_hi = hi_key / kTileN;
+  const int n_pages = (L + kBlockSize - 1) / kBlockSize;
+  const int32_t* bt = p.block_table + (size_t)b * p.max_blocks;
+  const size_t head_off = (size_t)h * 2 * kBlockSize * D;
+  const size_t blk_stride = (size_t)p.num_kv_heads * 2 * kBlockSize * D;
+
+  // ---- state ----------------------------------------------------------------
+  float m_run = kNegInfP;        // running max of this lane's query (log2 domain)
+  float l_run = 0.f;             // running denominator
+  f32x4 o[DB];                   // O[query 4g+i][16db + n]
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int t = t_lo; t <= t_hi; ++t) {
+    // ---- stage the tile's K (as bf16) and V (e4m3) rows in LDS ---------------
+    // zeros past the end of the sequence
+    __syncthreads();
+    constexpr int C16 = D / 16;                       // 16-byte chunks per cached row
+    for (int ci = threadIdx.x; ci < 2 * kTileN * C16; ci += 64 * kWaves) {
+      const int kv = ci / (kTileN * C16);
+      const int rem = ci % (kTileN * C16);
+      const int key = rem / C16;
+      const int c16 = rem % C16;
+      const int page = (t * kTileN + key) / kBlockSize;
+      uint4 val = make_uint4(0, 0, 0, 0);
+      if (page < n_pages) {
+        const uint8_t* src = p.cache + (size_t)bt[page] * blk_stride + head_off +
+                             (size_t)kv * kBlockSize * D + (key % kBlockSize) * D + c16 * 16;
+        val = *reinterpret_cast<const uint4*>(src);
+      }
+      if (kv == 0) {
+        const uint32_t w[4] = {val.x, val.y, val.z, val.w};
+        uint32_t o8[8];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          o8[2 * q4] = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16<false>(w[q4]));
+          o8[2 * q4 + 1] = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16<true>(w[q4]));
+        }
+        uint4* dst = reinterpret_cast<uint4*>(s_k + key * RSK + c16 * 32);
+        dst[0] = make_uint4(o8[0], o8[1], o8[2], o8[3]);
+        dst[1] = make_uint4(o8[4], o8[5], o8[6], o8[7]);
+      } else {
+        *reinterpret_cast<uint4*>(s_v + key * RSV + c16 * 16) = val;
+      }
+    }
+    __syncthreads();
+
+    // ---- S^T = K . Q^T : 8 blocks of 16 keys -----------------------------------
+    f32x4 s[8];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kq = 0; kq < KQ; ++kq) {
+        const uint4 a = *reinterpret_cast<const uint4*>(s_k + (16 * mb + n) * RSK +
+                                                         (kq * 32 + g * 8) * 2);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), qb[kq],
+                                                       acc, 0, 0, 0);
+      }
+      s[mb] = acc;
+    }
+
+    // ---- scale, mask, tile maximum ------------------------------------------
+    float tmax = kNegInfP;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = t * kTileN + 16 * mb + 4 * g + i;
+        const bool vis = row_ok && key <= pos && (p.window <= 0 || pos - key < p.window);
+        const float v = vis ? s[mb][i] * qk : kNegInfP;
+        s[mb][i] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    tmax = group4_max(tmax);
+    const float m_new = fmaxf(m_run, tmax);
+    const float ref = m_new > kNegInfP ? m_new : 0.f;
+    const float alpha = m_run > kNegInfP ? fast_exp2(m_run - m_new) : 0.f;
+
+    // ---- probabilities: fp32 sum, e4m3 operand -------------------------------
+    float psum = 0.f;
+    i32x8 pa;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      float pv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pv[i] = fast_exp2(s[mb][i] - ref);
+        psum += pv[i];
+      }
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);  // RNE
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], w, true);
+      pa[mb] = w;
+    }
+    psum = group4_sum(psum);
+    l_run = alpha * l_run + psum;
+    m_run = m_new;
+
+    // alpha of the four queries (4g + i) whose O rows this lane holds
+    float alpha_o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) alpha_o[i] = __shfl(alpha, 4 * g + i);
+
+    // ---- P~ . V~ per 16-column block -------------------------------------------
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      i32x8 vb;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        // row j = n/2 of read r is key kappa(g, 8r + j); lanes 2j, 2j+1 give
+        // the two 8-byte halves of the block's 16 columns
+        const int j = n >> 1;
+        const int key = 32 * r + 16 * (j >> 2) + 4 * g + (j & 3);
+        const i32x2 v2 = lds_read_tr8(s_v + key * RSV + 16 * db + (n & 1) * 8);
+        vb[2 * r] = v2[0];
+        vb[2 * r + 1] = v2[1];
+      }
+      if (p.accum_mode == 1) {
+        const f32x4 acc = mfma_fp8(pa, vb, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[db][i] = alpha_o[i] * o[db][i] + acc[i];
+      } else {
+        f32x4 c;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c[i] = alpha_o[i] * o[db][i];
+        o[db] = mfma_fp8(pa, vb, c);
+      }
+    }
+  }
+
+  // ---- epilogue: out = O * v_scale / l ---------------------------------------
+  const float vsc = p.v_scale[h];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float li = __shfl(l_run, 4 * g + i);
+    const int orow = q0 + wave * kWaveRows + 4 * g + i;
+    if (orow < T) {
+      const float sc = li > 0.f ? vsc / li : 0.f;
+      float* dst = p.out + ((size_t)(qs + orow) * p.num_q_heads + hq) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) dst[16 * db + n] = o[db][i] * sc;
+    }
+  }
+}
+
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
+  dim3 grid((p.max_q_len + kBlockM - 1) / kBlockM, p.num_q_heads, p.batch);
+  dim3 block(64 * kWaves);
+  switch (p.head_dim) {
+    case 64: hipLaunchKernelGGL(prefill_kernel<64>, grid, block, 0, stream, p); break;
+    case 128: hipLaunchKernelGGL(prefill_kernel<128>, grid, block, 0, stream, p); break;
+    case 256: hipLaunchKernelGGL(prefill_kernel<256>, grid, block, 0, stream, p); break;
+    default: return hipErrorNotSupported;
+  }
+  return hipGetLastError();
+}
 
 }  // namespace fa8

@@ -34,11 +34,18 @@ def metrics(gpu, ref):
     return max_abs, rel
 
 
-def assert_gate(gpu, ref, what, max_abs=MAX_ABS, rel_l2=REL_L2):
+def assert_gate(gpu, ref, what, max_abs=MAX_ABS, rel_l2=REL_L2, slack=None):
+    """Gate: relative L2 of the raw difference, and max |gpu - ref| beyond
+    ``slack`` (the oracle's per-element allowance for e4m3 roundings of p
+    that a float32 kernel may legitimately take the other way; None = 0)."""
     ma, rl = metrics(gpu, ref)
-    log(f"  {what}: max_abs={ma:.3e} rel_l2={rl:.3e}")
+    diff = np.abs(np.asarray(gpu, np.float64) - np.asarray(ref, np.float64))
+    excess = diff if slack is None else np.maximum(diff - slack, 0.0)
+    me = float(excess.max()) if excess.size else 0.0
+    extra = "" if slack is None else f" beyond-flip-allowance={me:.3e} (max allowance {float(np.max(slack)):.3e})"
+    log(f"  {what}: max_abs={ma:.3e} rel_l2={rl:.3e}{extra}")
     assert np.all(np.isfinite(gpu)), f"{what}: non-finite GPU output"
-    assert ma <= max_abs and rl <= rel_l2, f"{what}: max_abs={ma:.3e} rel_l2={rl:.3e}"
+    assert me <= max_abs and rl <= rel_l2, f"{what}: max_abs={ma:.3e} excess={me:.3e} rel_l2={rl:.3e}"
 
 
 def dev(x, dtype=None):
@@ -134,3 +141,78 @@ class DecodeCase:
             outs.append(o)
             qheads += list(range(h * G, (h + 1) * G))
         return np.concatenate(outs, axis=1), qheads
+
+
+class PrefillCase:
+    """Chunked prefill over a paged e4m3 cache: sequence b has context
+    lens[b] whose last qlens[b] tokens are the queries (packed by cu)."""
+
+    def __init__(self, qlens, lens, Hq, Hkv, D, seed=0, window=0, q_zero=False,
+                 q_scale="absmax"):
+        import torch
+        import attention_fp8_quantized_amd as fa
+        self.qlens = np.asarray(qlens, dtype=np.int32)
+        self.lens = np.asarray(lens, dtype=np.int32)
+        assert np.all(self.lens >= self.qlens)
+        self.B = len(self.lens)
+        self.Hq, self.Hkv, self.D, self.window = Hq, Hkv, D, window
+        g = np.random.default_rng(seed)
+        self.bt, self.nblocks = W.block_table(g, self.lens)
+        N = int(self.lens.sum())
+        k = W.normal(W.rng(seed, 0, W.K), (N, Hkv, D))
+        v = W.normal(W.rng(seed, 0, W.V), (N, Hkv, D))
+        self.ks, self.vs = W.absmax_scales(k), W.absmax_scales(v)
+        self.slots = W.all_slots(self.bt, self.lens)
+        need = W.blocks_needed(self.lens)
+        for b, nb in enumerate(need):
+            assert np.all((self.bt[b, :nb] >= 0) & (self.bt[b, :nb] < self.nblocks))
+        assert self.slots.max() < self.nblocks * 16
+        self.cu = np.concatenate([[0], np.cumsum(self.qlens)]).astype(np.int32)
+        Tq = int(self.cu[-1])
+        qf = np.zeros((Tq, Hq, D), np.float32) if q_zero else W.normal(W.rng(seed, 0, W.Q), (Tq, Hq, D))
+        qb, self.q = W.bf16_values(qf)
+        if q_scale == "absmax":
+            self.qs = np.array([max(float(np.abs(self.q).max()), 1e-30) / 448.0], np.float32)
+        else:
+            self.qs = np.array([q_scale], np.float32)
+        self.k, self.v = k, v
+        self.cache = fa.new_cache(self.nblocks, Hkv, D, "e4m3")
+        self.cache.view(torch.uint8).fill_(0)
+        fa.cache_write(dev(k), dev(v), dev(self.slots), dev(self.ks), dev(self.vs), self.cache)
+        self.q_dev = qb.cuda()
+        self.dev = {n: dev(a) for n, a in dict(cu=self.cu, bt=self.bt, lens=self.lens,
+                                                qs=self.qs, ks=self.ks, vs=self.vs).items()}
+        self.sm = np.float32(1.0 / math.sqrt(D))
+        self._oracle_cache = None
+
+    def run_gpu(self, accum_mode=1):
+        import torch
+        import attention_fp8_quantized_amd as fa
+        d = self.dev
+        out = fa.prefill_attention(self.q_dev, d["cu"], self.cache, d["bt"], d["lens"], d["qs"],
+                                   d["ks"], d["vs"], float(self.sm), int(self.qlens.max()),
+                                   window=self.window, accum_mode=accum_mode)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+    def oracle_cache(self):
+        if self._oracle_cache is None:
+            c = OQ.new_cache(self.nblocks, self.Hkv, self.D, "e4m3")
+            self._oracle_cache = OQ.cache_write(c, self.k, self.v, self.slots, self.ks, self.vs,
+                                                "e4m3")
+        return self._oracle_cache
+
+    # float32 score and exp2 error of the kernel, relative, with a 4x margin
+    FLIP_TOL = 4e-6
+
+    def oracle(self, rows=None, exact=False):
+        """(reference, flip allowance) for the mirror; the reference alone
+        for the unquantised-P reference (exact=True)."""
+        import attention_fp8_quantized_amd as fa
+        from oracle import attention as OA
+        args = (self.q, self.cu, self.oracle_cache(), self.bt, self.lens, self.qs[0], self.ks,
+                self.vs, self.sm, self.window)
+        if exact:
+            return OA.prefill_exact(*args, rows=rows)
+        return OA.prefill_mirror(*args, kv_tile=fa.prefill_kv_tile(self.D), rows=rows,
+                                 flip_tol=self.FLIP_TOL)
