@@ -52,6 +52,8 @@ _SIGNATURES = {
     "fa8_prefill_attention": (_I32, [_VP, _VP, _I32, _I32, _I32, _VP, _I64, _I32, _I32,
                                      _VP, _I32, _VP, _VP, _VP, _VP, _F32, _I32, _I32,
                                      _VP, _VP]),
+    "fa8_stream_read": (_I32, [_VP, _SZ, _VP, _VP]),
+    "fa8_stream_copy": (_I32, [_VP, _VP, _SZ, _VP]),
     "fa8_status_string": (ctypes.c_char_p, [_I32]),
     "fa8_last_error": (ctypes.c_char_p, []),
 }
@@ -254,3 +256,26 @@ def prefill_attention(q, cu_q_lens, cache, block_table, seq_lens, q_scale, k_sca
         _ptr(k_scale), _ptr(v_scale), float(sm_scale), int(window), int(accum_mode),
         _ptr(out), _stream(cache)))
     return out
+
+
+def stream_read(src, sink):
+    """Read all of ``src`` (a contiguous CUDA tensor, nbytes % 16 == 0) once;
+    ``sink`` is a CUDA tensor of >= 4 bytes."""
+    _require(src, "src")
+    _require(sink, "sink", device=src.device)
+    if sink.numel() * sink.element_size() < 4:
+        raise ValueError("sink must hold >= 4 bytes")
+    lib = load()
+    _check(lib.fa8_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                               _stream(src)))
+
+
+def stream_copy(dst, src):
+    """dst <- src bytewise (contiguous CUDA tensors of equal byte size)."""
+    _require(src, "src")
+    _require(dst, "dst", device=src.device)
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise ValueError("dst and src must have the same byte size")
+    lib = load()
+    _check(lib.fa8_stream_copy(_ptr(dst), _ptr(src), n, _stream(src)))

@@ -259,4 +259,24 @@ fa8_status fa8_prefill_attention(const void* q, const int32_t* cu_q_lens, int32_
   return ok();
 }
 
+fa8_status fa8_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (bytes % 16 != 0) return fail(FA8_EINVAL, "stream_read: bytes must be a multiple of 16");
+  if (bytes == 0) return ok();
+  if (!src || !sink) return fail(FA8_EINVAL, "stream_read: null pointer argument");
+  const hipError_t e = fa8::launch_stream_read(src, bytes, sink, device_cu_count(),
+                                               reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "stream_read launch");
+  return ok();
+}
+
+fa8_status fa8_stream_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  if (bytes % 16 != 0) return fail(FA8_EINVAL, "stream_copy: bytes must be a multiple of 16");
+  if (bytes == 0) return ok();
+  if (!src || !dst) return fail(FA8_EINVAL, "stream_copy: null pointer argument");
+  const hipError_t e = fa8::launch_stream_copy(dst, src, bytes, device_cu_count(),
+                                               reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "stream_copy launch");
+  return ok();
+}
+
 }  // extern "C"

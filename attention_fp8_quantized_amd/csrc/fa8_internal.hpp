@@ -64,4 +64,10 @@ struct PrefillParams {
 int prefill_kv_tile(int head_dim);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 
+// bandwidth yardsticks (stream_bench.hip)
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int cus,
+                              hipStream_t stream);
+hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, int cus,
+                              hipStream_t stream);
+
 }  // namespace fa8

@@ -1,32 +1,45 @@
-"""Benchmark: FP8 paged-KV decode on one MI355X.
+"""Benchmark: FP8 paged-KV attention on one MI355X.
 
-Workload (one step): a Llama-3.1-8B-shaped decode step over 32 independent
-layers -- 32 query / 8 KV heads, head_dim 128, block size 16, batch 1,
-32k-token context, K/V ~ N(0,1) with 1% outlier channels x20 and per-KV-head
-absmax/448 scales.  Per layer the step writes the current token's K/V into
-the FP8 cache (cache_write) and runs decode attention over the whole context.
-The 32 layer caches (2.1 GB) are distinct so the 256 MB last-level cache
-cannot serve repeated reads.
+Headline workload (one step): a Llama-3.1-8B-shaped decode step over 32
+distinct layers -- 32 query / 8 KV heads, head_dim 128, block size 16,
+batch 1, 32k-token context, K/V ~ N(0,1) with 1% outlier channels x20 and
+per-KV-head absmax/448 scales.  Per layer the step writes the current token's
+K/V into the FP8 cache (cache_write) and runs decode attention over the whole
+context.  The 32 layer caches (2.1 GB) are distinct, so the 256 MB
+last-level cache cannot serve repeated reads.
 
 Printed: one JSON line with
-  value      algorithmic KV GB/s of the whole step (decode + cache write)
-  roofline   the decode kernel alone, timed with HIP events on its stream,
-             against the 8 TB/s HBM peak
-  slope      decode time per context token for the FP8 and the BF16 cache
-             (same kernel), fitted over contexts {1k, 8k, 32k, 128k} as
-             t = slope * ctx + intercept, and their ratio
-  prefill    (when built) head_dim-256 FP8 prefill chunk throughput vs the
-             5 PFLOP/s dense FP8 MFMA peak
-  cpu_baseline  the fp64 NumPy oracle decoding one layer of the same
-             workload on the host cores
+  value         algorithmic bytes of the whole step (decode + cache write)
+                per second of step time
+  roofline      the decode kernel alone: algorithmic bytes per launch over
+                its average launch time (HIP events on the kernel's stream
+                around the timed steps' decode launches run back to back),
+                against the 8 TB/s HBM peak; traffic = HBM bytes per launch
+                from calibrated hardware counters when they were taken on
+                the current decode sources
+  stream_read   a plain streaming read of the same bytes per launch on the
+                same device (the achievable read rate decode is compared to)
+  slope         decode time per context token, FP8 vs BF16 cache (same
+                kernel), fitted over contexts {1k, 8k, 32k, 128k}
+  loaded        8 sequences of U{18000..22000} tokens, 32 distinct layers
+  hybrid        gpt-oss-20b-shaped 24-layer step (12 full + 12 128-token
+                sliding-window layers), all-BF16 / all-FP8 / FP8 skip-SW
+  hd256         8/1 heads, head_dim 256: 32k causal FP8 prefill chunk
+                (two-level and one-level accumulation) against the 5 PFLOP/s
+                dense FP8 MFMA peak, a 128k fill in four 32k chunks, decode
+                at 128k
+  cpu_baseline  the fp64 NumPy oracle decoding one layer of the headline
+                workload on the host cores (bounded sample)
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--quick]
 """
 
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -38,6 +51,11 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP8_MFMA_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, TFLOP/s
 
+# HBM traffic of the decode kernel, measured with hardware counters; valid
+# only while the decode sources hash to the value recorded beside it
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_llama_ctx32k_traffic.md")
+DECODE_SOURCES = ["decode.hip", "fa8_device.hpp", "fa8_internal.hpp"]
+
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
@@ -47,13 +65,15 @@ def log(msg):
 # algorithmic work
 # ---------------------------------------------------------------------------
 
-def decode_bytes(B, Hq, Hkv, D, ctx, elem):
+def decode_bytes(B, Hq, Hkv, D, ctx, elem, window=0):
     """Bytes decode must move: K and V of every visible token, q in (bf16),
-    out (fp32), the block-table entries and the two scale vectors."""
-    n = ctx
-    kv = B * n * Hkv * D * 2 * elem
+    out (fp32), the block-table entries read and the two scale vectors.
+    ``ctx`` is an int or a per-sequence list."""
+    lens = [ctx] * B if np.isscalar(ctx) else list(ctx)
+    n = [min(L, window) if window > 0 else L for L in lens]
+    kv = sum(n) * Hkv * D * 2 * elem
     qo = B * Hq * D * (2 + 4)
-    bt = B * math.ceil(n / 16) * 4
+    bt = sum(math.ceil(x / 16) for x in n) * 4
     sc = 8 * Hkv
     return kv + qo + bt + sc
 
@@ -62,28 +82,54 @@ def cache_write_bytes(N, Hkv, D, in_bytes, elem):
     return N * Hkv * D * 2 * (in_bytes + elem)
 
 
+def prefill_flops(T, P, Hq, D):
+    """4*D*Hq per visible (query, key) pair, causal: T*P + T(T+1)/2 pairs."""
+    return 4.0 * D * Hq * (T * P + T * (T + 1) / 2)
+
+
+def decode_source_hash():
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "attention_fp8_quantized_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed counter summary, or
+    None when it is absent or was taken on different decode sources."""
+    try:
+        with open(TRAFFIC_PROFILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    src = re.search(r"decode sources sha256\[:16\]:\s*([0-9a-f]+)", text)
+    val = re.search(r"HBM bytes per launch:\s*([0-9.eE+]+)", text)
+    if not src or not val or src.group(1) != decode_source_hash():
+        return None
+    return float(val.group(1))
+
+
 # ---------------------------------------------------------------------------
 # synthetic caches on the device
 # ---------------------------------------------------------------------------
 
 def fill_pool(fa, torch, pool_blocks, Hkv, D, cache_dtype, seed, outliers=True):
     """A pool of blocks filled through the library's cache_write from
-    N(0,1) K/V (seeded device RNG) with 1% outlier channels x20 and
-    absmax/448 per-head scales.  Returns (cache, k_scale, v_scale)."""
+    N(0,1) K/V (seeded device RNG), optionally with 1% outlier channels x20,
+    and absmax/448 per-head scales over the pool.  Returns
+    (cache, k_scale, v_scale)."""
     dev = torch.device("cuda")
     cache = fa.new_cache(pool_blocks, Hkv, D, cache_dtype, device=dev)
     gen = torch.Generator(device=dev)
     gen.manual_seed(seed)
-    n_out = int(round(0.01 * Hkv * D))
-    pick_k = torch.randperm(Hkv * D, generator=gen, device=dev)[:n_out]
-    pick_v = torch.randperm(Hkv * D, generator=gen, device=dev)[:n_out]
     mul_k = torch.ones(Hkv * D, device=dev)
-    mul_k[pick_k] = 20.0
     mul_v = torch.ones(Hkv * D, device=dev)
-    mul_v[pick_v] = 20.0
+    if outliers:
+        n_out = int(round(0.01 * Hkv * D))
+        mul_k[torch.randperm(Hkv * D, generator=gen, device=dev)[:n_out]] = 20.0
+        mul_v[torch.randperm(Hkv * D, generator=gen, device=dev)[:n_out]] = 20.0
     mul_k, mul_v = mul_k.view(1, Hkv, D), mul_v.view(1, Hkv, D)
-    # scales: absmax over the whole pool's draws; N(0,1) absmax over this
-    # many draws is ~5.5-6, x20 outliers dominate: use the outlier-aware max
     total = pool_blocks * 16
     chunk = 1 << 16
     amax_k = torch.zeros(Hkv, device=dev)
@@ -108,49 +154,138 @@ def fill_pool(fa, torch, pool_blocks, Hkv, D, cache_dtype, seed, outliers=True):
     return cache, ks, vs
 
 
-def layer_tables(torch, layers, blocks_per_layer, pool_blocks, seed):
-    """int32 [layers][blocks_per_layer]: each layer owns distinct pool blocks
-    (a seeded permutation, so logical pages are never in physical order)."""
+def layer_tables(torch, layers, lens, pool_blocks, seed, window=0):
+    """int32 [layers][B][max_blocks]: every layer and sequence owns distinct
+    pool blocks (a seeded permutation, never in physical order).  With a
+    window, only the pages the window can reach get their own blocks; the
+    others point at block 0 and are never read."""
     g = torch.Generator()
     g.manual_seed(seed)
-    need = layers * blocks_per_layer
-    assert need <= pool_blocks
+    B = len(lens)
+    width = max(math.ceil(L / 16) for L in lens)
+    first = [max(0, L - window) // 16 if window > 0 else 0 for L in lens]
+    own = [math.ceil(L / 16) - f for L, f in zip(lens, first)]
+    need = layers * sum(own)
+    assert need <= pool_blocks, (need, pool_blocks)
     perm = torch.randperm(pool_blocks, generator=g)[:need].to(torch.int32)
-    return perm.view(layers, blocks_per_layer).cuda()
+    bt = torch.zeros((layers, B, width), dtype=torch.int32)
+    at = 0
+    for li in range(layers):
+        for b in range(B):
+            bt[li, b, first[b]:first[b] + own[b]] = perm[at:at + own[b]]
+            at += own[b]
+    return bt.cuda()
 
 
-# ---------------------------------------------------------------------------
-# measurements
-# ---------------------------------------------------------------------------
+def pool_blocks_for(layers, lens, window=0):
+    first = [max(0, L - window) // 16 if window > 0 else 0 for L in lens]
+    return layers * sum(math.ceil(L / 16) - f for L, f in zip(lens, first))
 
-def time_decode(fa, torch, cache, tables, ks, vs, q, ctx, D, reps, splits=0):
-    """Average time (ms) of one decode call, cycling through the layers'
-    block tables; HIP events on the stream the kernel is launched on."""
-    B = q.shape[0]
-    lens = torch.full((B,), ctx, dtype=torch.int32, device="cuda")
-    layers = tables.shape[0]
-    S = splits or fa.decode_num_splits(B, cache.shape[1], ctx)
-    ws = fa.new_decode_workspace(fa.decode_workspace_bytes(B, q.shape[1], D, S))
-    out = torch.empty((B, q.shape[1], D), dtype=torch.float32, device="cuda")
-    sm = 1.0 / math.sqrt(D)
-    bts = [tables[i:i + 1].expand(B, -1).contiguous() for i in range(layers)]
-    for i in range(min(layers, 4)):      # warm-up
-        fa.decode_attention(q, cache, bts[i], lens, ks, vs, sm, ctx, num_splits=S,
-                            out=out, workspace=ws)
-    stream = torch.cuda.current_stream()
+
+class DecodeLayers:
+    """``layers`` distinct decode layers of one shape, their caches in one
+    pool, called back to back.  Each call of run() can record HIP events
+    around every decode launch."""
+
+    def __init__(self, fa, torch, layers, lens, Hq, Hkv, D, cache_dtype, seed, window=0,
+                 outliers=True, splits=0):
+        self.fa, self.torch = fa, torch
+        self.layers, self.lens, self.window = layers, list(lens), window
+        self.B, self.Hq, self.Hkv, self.D, self.cd = len(lens), Hq, Hkv, D, cache_dtype
+        self.elem = 1 if cache_dtype == "e4m3" else 2
+        pool = pool_blocks_for(layers, self.lens, window)
+        self.cache, self.ks, self.vs = fill_pool(fa, torch, pool, Hkv, D, cache_dtype, seed,
+                                                 outliers)
+        tables = layer_tables(torch, layers, self.lens, pool, seed + 1, window)
+        self.bts = [tables[i].contiguous() for i in range(layers)]
+        dev = torch.device("cuda")
+        gq = torch.Generator(device=dev)
+        gq.manual_seed(seed + 2)
+        self.qs = [torch.randn((self.B, Hq, D), generator=gq, device=dev).to(torch.bfloat16)
+                   for _ in range(layers)]
+        self.knew = [torch.randn((self.B, Hkv, D), generator=gq, device=dev)
+                     for _ in range(layers)]
+        self.vnew = [torch.randn((self.B, Hkv, D), generator=gq, device=dev)
+                     for _ in range(layers)]
+        self.lens_dev = torch.tensor(self.lens, dtype=torch.int32, device=dev)
+        # slot of each sequence's current token (position L-1) per layer
+        last = torch.tensor([(L - 1) // 16 for L in self.lens], dtype=torch.int64, device=dev)
+        off = torch.tensor([(L - 1) % 16 for L in self.lens], dtype=torch.int64, device=dev)
+        ar = torch.arange(self.B, device=dev)
+        self.slot_new = [(self.bts[i][ar, last].to(torch.int64) * 16 + off).contiguous()
+                         for i in range(layers)]
+        self.max_len = max(self.lens)
+        self.S = splits or fa.decode_num_splits(self.B, Hkv, self.max_len, window)
+        self.ws = fa.new_decode_workspace(fa.decode_workspace_bytes(self.B, Hq, D, self.S))
+        self.out = torch.empty((self.B, Hq, D), dtype=torch.float32, device=dev)
+        self.sm = 1.0 / math.sqrt(D)
+        self.bytes_per_layer = decode_bytes(self.B, Hq, Hkv, D, self.lens, self.elem, window)
+        self.write_bytes = cache_write_bytes(self.B, Hkv, D, 4, self.elem)
+
+    def run_layer(self, i, write=True, events=None):
+        fa = self.fa
+        if write:
+            fa.cache_write(self.knew[i], self.vnew[i], self.slot_new[i], self.ks, self.vs,
+                           self.cache)
+        if events is not None:
+            events[0].record()
+        fa.decode_attention(self.qs[i], self.cache, self.bts[i], self.lens_dev, self.ks,
+                            self.vs, self.sm, self.max_len, window=self.window,
+                            num_splits=self.S, out=self.out, workspace=self.ws)
+        if events is not None:
+            events[1].record()
+
+    def free(self):
+        del self.cache, self.bts, self.ws
+        self.torch.cuda.empty_cache()
+
+
+def timed(torch, fn, reps):
+    """Average ms of fn() over reps calls, HIP events on the current stream
+    (the stream every launch of this file goes to)."""
+    fn()
+    torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    n = 0
+    e0.record()
     for _ in range(reps):
-        for i in range(layers):
-            fa.decode_attention(q, cache, bts[i], lens, ks, vs, sm, ctx, num_splits=S,
-                                out=out, workspace=ws)
-            n += 1
-    e1.record(stream)
+        fn()
+    e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / n, S
+    return e0.elapsed_time(e1) / reps
+
+
+def decode_only_ms(torch, dl, reps):
+    """Per-layer ms of decode alone, cycling through the distinct layers."""
+    def all_layers():
+        for i in range(dl.layers):
+            dl.run_layer(i, write=False)
+    return timed(torch, all_layers, reps) / dl.layers
+
+
+# ---------------------------------------------------------------------------
+# measurement legs
+# ---------------------------------------------------------------------------
+
+def measure_stream_read(fa, torch, per_launch, total=4 << 30, reps=64):
+    """Plain streaming read of ``per_launch`` bytes per launch over distinct
+    buffers (``total`` bytes in all, beyond the last-level cache)."""
+    per_launch = (per_launch // 16) * 16
+    buf = torch.empty(total, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    chunks = max(1, total // per_launch)
+    views = [buf[i * per_launch:(i + 1) * per_launch] for i in range(chunks)]
+    state = {"i": 0}
+
+    def one():
+        fa.stream_read(views[state["i"] % chunks], sink)
+        state["i"] += 1
+    ms = timed(torch, one, reps)
+    del buf, views
+    torch.cuda.empty_cache()
+    return {"bytes_per_launch": per_launch, "us": round(ms * 1e3, 3),
+            "gbs": round(per_launch / (ms * 1e-3) / 1e9, 1)}
 
 
 def slope_fit(ctxs, times):
@@ -159,37 +294,127 @@ def slope_fit(ctxs, times):
     return float(slope), float(icpt)
 
 
-def measure_slope(fa, torch, Hq, Hkv, D, contexts, min_pool_bytes, reps):
+def measure_slope(fa, torch, Hq, Hkv, D, contexts, min_bytes=1.1e9, reps=3):
     """Per-layer decode time at each context for the FP8 and the BF16 cache
-    (same kernel), over enough distinct layers that the working set exceeds
-    the last-level cache.  Returns dict with times, slopes and ratio."""
+    (same kernel), over enough distinct layers (>= 1.1 GB, >= 4) that the
+    last-level cache cannot serve them.  Returns times, slopes, ratio."""
     res = {}
-    q = torch.randn((1, Hq, D), device="cuda").to(torch.bfloat16)
     for cd, elem in (("e4m3", 1), ("bf16", 2)):
-        blocks_max = math.ceil(max(contexts) / 16)
-        page_bytes = 2 * Hkv * 16 * D * elem
-        pool = max(math.ceil(min_pool_bytes / page_bytes), 4 * blocks_max)
-        cache, ks, vs = fill_pool(fa, torch, pool, Hkv, D, cd, seed=2000 + elem)
         times = []
         for ctx in contexts:
-            bpl = math.ceil(ctx / 16)
-            layers = max(1, min(pool // bpl, 256))
-            tables = layer_tables(torch, layers, bpl, pool, seed=ctx)
-            t, S = time_decode(fa, torch, cache, tables, ks, vs, q, ctx, D,
-                               reps=max(1, reps * 32 // layers))
+            per = decode_bytes(1, Hq, Hkv, D, ctx, elem)
+            layers = int(min(256, max(4, math.ceil(min_bytes / per))))
+            dl = DecodeLayers(fa, torch, layers, [ctx], Hq, Hkv, D, cd, seed=2000 + ctx + elem)
+            t = decode_only_ms(torch, dl, reps=max(1, reps * 32 // layers))
             times.append(t)
             log(f"  slope point {cd} ctx={ctx}: {t * 1e3:.2f} us/layer "
-                f"({decode_bytes(1, Hq, Hkv, D, ctx, elem) / t / 1e6:.0f} GB/s, S={S}, "
-                f"{layers} layers)")
+                f"({per / t / 1e6:.0f} GB/s, S={dl.S}, {layers} layers)")
+            dl.free()
         s, i = slope_fit(contexts, times)
-        res[cd] = dict(ms_per_layer=times, slope_ms_per_token=s, intercept_ms=i)
-        del cache
-        torch.cuda.empty_cache()
+        res[cd] = dict(ms_per_layer=[round(x, 6) for x in times], slope_ms_per_token=s,
+                       intercept_ms=i)
     res["ratio_fp8_over_bf16"] = res["e4m3"]["slope_ms_per_token"] / res["bf16"]["slope_ms_per_token"]
     s8, i8 = res["e4m3"]["slope_ms_per_token"], res["e4m3"]["intercept_ms"]
     s16, i16 = res["bf16"]["slope_ms_per_token"], res["bf16"]["intercept_ms"]
     res["break_even_tokens"] = (i8 - i16) / (s16 - s8) if s16 != s8 else None
     res["contexts"] = list(contexts)
+    return res
+
+
+def measure_loaded(fa, torch, reps=5):
+    """8 sequences of U{18000..22000} tokens, 32/8 heads, hd128, FP8, 32
+    distinct layers back to back (cache write + decode per layer)."""
+    import workloads as W
+    lens = [int(x) for x in W.uniform_lengths(W.rng(3, 0, W.LENGTHS), 8, 18000, 22000)]
+    dl = DecodeLayers(fa, torch, 32, lens, 32, 8, 128, "e4m3", seed=3000)
+
+    def step():
+        for i in range(dl.layers):
+            dl.run_layer(i)
+    ms = timed(torch, step, reps)
+    dec = decode_only_ms(torch, dl, reps)
+    total = dl.layers * (dl.bytes_per_layer + dl.write_bytes)
+    res = {"lens": lens, "layers": 32, "ms_per_step": round(ms, 4),
+           "gbs": round(total / (ms * 1e-3) / 1e9, 1),
+           "decode_us_per_layer": round(dec * 1e3, 2),
+           "decode_gbs": round(dl.bytes_per_layer / (dec * 1e-3) / 1e9, 1), "splits": dl.S}
+    dl.free()
+    return res
+
+
+def measure_hybrid(fa, torch, reps=5):
+    """gpt-oss-20b-shaped step: 24 layers, 12 full-attention and 12
+    128-token sliding-window, 64/8 heads, hd64, 8 x 20000 tokens.  Variants:
+    all BF16, all FP8, FP8 full layers with BF16 sliding-window layers."""
+    lens = [20000] * 8
+    res = {}
+    for name, full_cd, sw_cd in (("all-bf16", "bf16", "bf16"), ("all-fp8", "e4m3", "e4m3"),
+                                 ("fp8-skip-sw", "e4m3", "bf16")):
+        full = DecodeLayers(fa, torch, 12, lens, 64, 8, 64, full_cd, seed=4000)
+        sw = DecodeLayers(fa, torch, 12, lens, 64, 8, 64, sw_cd, seed=4100, window=128)
+
+        def step():
+            for i in range(12):
+                sw.run_layer(i)
+                full.run_layer(i)
+        ms = timed(torch, step, reps)
+        total = 12 * (full.bytes_per_layer + full.write_bytes + sw.bytes_per_layer +
+                      sw.write_bytes)
+        res[name] = {"ms_per_step": round(ms, 4), "gbs": round(total / (ms * 1e-3) / 1e9, 1)}
+        log(f"  hybrid {name}: {ms:.3f} ms/step")
+        full.free()
+        sw.free()
+    return res
+
+
+def measure_hd256(fa, torch, reps=3):
+    """8/1 heads, head_dim 256, FP8: causal prefill of a 32k chunk (P = 0,
+    accum_mode 1 and 0), a 128k fill in four 32k chunks, and decode at 128k
+    over 16 distinct layers."""
+    Hq, Hkv, D, T = 8, 1, 256, 32768
+    dev = torch.device("cuda")
+    L = 4 * T
+    nb = L // 16
+    cache, ks, vs = fill_pool(fa, torch, nb, Hkv, D, "e4m3", seed=5000, outliers=False)
+    bt = torch.randperm(nb, generator=torch.Generator().manual_seed(5)).to(torch.int32)
+    bt = bt.view(1, nb).cuda()
+    gq = torch.Generator(device=dev)
+    gq.manual_seed(5001)
+    q = torch.randn((T, Hq, D), generator=gq, device=dev).to(torch.bfloat16)
+    qs = (q.float().abs().amax() / 448.0).view(1).contiguous()
+    cu = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    out = torch.empty((T, Hq, D), dtype=torch.float32, device=dev)
+    sm = 1.0 / math.sqrt(D)
+    res = {"prefill_32k": []}
+    lens = torch.tensor([T], dtype=torch.int32, device=dev)
+    fl = prefill_flops(T, 0, Hq, D)
+    for mode in (1, 0):
+        ms = timed(torch, lambda: fa.prefill_attention(q, cu, cache, bt, lens, qs, ks, vs, sm, T,
+                                                       accum_mode=mode, out=out), reps)
+        tf = fl / (ms * 1e-3) / 1e12
+        res["prefill_32k"].append({"accum_mode": mode, "ms": round(ms, 4),
+                                   "tflops": round(tf, 1),
+                                   "frac_fp8_peak": round(tf / FP8_MFMA_PEAK_TFLOPS, 4)})
+        log(f"  prefill 32k accum_mode={mode}: {ms:.3f} ms, {tf:.0f} TFLOP/s")
+    chunk_lens = [torch.tensor([T * (c + 1)], dtype=torch.int32, device=dev) for c in range(4)]
+
+    def fill():
+        for c in range(4):
+            fa.prefill_attention(q, cu, cache, bt, chunk_lens[c], qs, ks, vs, sm, T, out=out)
+    ms = timed(torch, fill, 1)
+    fl = sum(prefill_flops(T, c * T, Hq, D) for c in range(4))
+    tf = fl / (ms * 1e-3) / 1e12
+    res["fill_128k_4x32k"] = {"ms": round(ms, 3), "tflops": round(tf, 1),
+                              "frac_fp8_peak": round(tf / FP8_MFMA_PEAK_TFLOPS, 4)}
+    log(f"  128k fill: {ms:.2f} ms, {tf:.0f} TFLOP/s")
+    del cache, out, q
+    torch.cuda.empty_cache()
+    dl = DecodeLayers(fa, torch, 16, [L], Hq, Hkv, D, "e4m3", seed=5100, outliers=False)
+    dec = decode_only_ms(torch, dl, reps)
+    res["decode_128k"] = {"us_per_layer": round(dec * 1e3, 2),
+                          "gbs": round(dl.bytes_per_layer / (dec * 1e-3) / 1e9, 1),
+                          "splits": dl.S}
+    dl.free()
     return res
 
 
@@ -233,37 +458,15 @@ def cpu_baseline(Hq, Hkv, D, ctx, budget_s=10.0):
                       f"BLAS threads {blas_threads}"}
 
 
-def measure_prefill(fa, torch, T=32768, Hq=8, Hkv=1, D=256, reps=3, accum_mode=1):
-    """Causal prefill chunk of T tokens (P = 0) on the head_dim-256 shape."""
-    dev = torch.device("cuda")
-    nb = math.ceil(T / 16)
-    cache, ks, vs = fill_pool(fa, torch, nb, Hkv, D, "e4m3", seed=5000, outliers=False)
-    bt = torch.randperm(nb, generator=torch.Generator().manual_seed(5)).to(torch.int32)
-    bt = bt.view(1, nb).cuda()
-    q = torch.randn((T, Hq, D), device=dev).to(torch.bfloat16)
-    qs = (q.float().abs().amax() / 448.0).view(1).contiguous()
-    cu = torch.tensor([0, T], dtype=torch.int32, device=dev)
-    lens = torch.tensor([T], dtype=torch.int32, device=dev)
-    out = torch.empty((T, Hq, D), dtype=torch.float32, device=dev)
-    sm = 1.0 / math.sqrt(D)
-    fa.prefill_attention(q, cu, cache, bt, lens, qs, ks, vs, sm, T, accum_mode=accum_mode,
-                         out=out)
-    stream = torch.cuda.current_stream()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
+def copy_calibration(fa, torch, nbytes=256 << 20, reps=4):
+    """Launches of the plain copy kernel on ``nbytes`` (reads and writes
+    nbytes each), for calibrating hardware byte counters."""
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
     for _ in range(reps):
-        fa.prefill_attention(q, cu, cache, bt, lens, qs, ks, vs, sm, T,
-                             accum_mode=accum_mode, out=out)
-    e1.record(stream)
+        fa.stream_copy(dst, src)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    pairs = T * (T + 1) / 2
-    flops = 4.0 * D * Hq * pairs
-    return {"T": T, "heads": f"{Hq}/{Hkv}", "head_dim": D, "accum_mode": accum_mode,
-            "ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 2),
-            "frac_fp8_peak": round(flops / ms / 1e9 / FP8_MFMA_PEAK_TFLOPS, 4)}
+    log(f"copy calibration: {reps} x stream_copy of {nbytes} bytes")
 
 
 # ---------------------------------------------------------------------------
@@ -276,13 +479,14 @@ def main():
     ap.add_argument("--ctx", type=int, default=32768)
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--splits", type=int, default=0)
-    ap.add_argument("--quick", action="store_true", help="skip slope, prefill and CPU legs")
+    ap.add_argument("--quick", action="store_true",
+                    help="headline step and its roofline only")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also launch the plain copy kernel (for counter calibration)")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-slope", action="store_true")
-    ap.add_argument("--no-prefill", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
@@ -292,63 +496,51 @@ def main():
     torch.cuda.init()
 
     B, Hq, Hkv, D, ctx, layers = 1, 32, 8, 128, args.ctx, args.layers
-    bpl = math.ceil(ctx / 16)
-    pool = bpl * layers
-    log(f"filling {layers} FP8 layers x {ctx} tokens ({pool * 2 * Hkv * 16 * D / 1e9:.2f} GB)")
-    cache, ks, vs = fill_pool(fa, torch, pool, Hkv, D, "e4m3", seed=1000)
-    tables = layer_tables(torch, layers, bpl, pool, seed=1)
-    dev = torch.device("cuda")
-    gq = torch.Generator(device=dev)
-    gq.manual_seed(3)
-    qs = [torch.randn((B, Hq, D), generator=gq, device=dev).to(torch.bfloat16)
-          for _ in range(layers)]
-    knew = [torch.randn((B, Hkv, D), generator=gq, device=dev) for _ in range(layers)]
-    vnew = [torch.randn((B, Hkv, D), generator=gq, device=dev) for _ in range(layers)]
-    lens = torch.full((B,), ctx, dtype=torch.int32, device=dev)
-    bts = [tables[i:i + 1].contiguous() for i in range(layers)]
-    # the current token (position ctx-1) of each layer
-    slot_new = [(tables[i, (ctx - 1) // 16].to(torch.int64) * 16 + (ctx - 1) % 16).view(1)
-                for i in range(layers)]
-    S = args.splits or fa.decode_num_splits(B, Hkv, ctx)
-    ws = fa.new_decode_workspace(fa.decode_workspace_bytes(B, Hq, D, S))
-    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
-    sm = 1.0 / math.sqrt(D)
+    log(f"filling {layers} FP8 layers x {ctx} tokens")
+    dl = DecodeLayers(fa, torch, layers, [ctx], Hq, Hkv, D, "e4m3", seed=1000,
+                      splits=args.splits)
 
     def step():
         for i in range(layers):
-            fa.cache_write(knew[i], vnew[i], slot_new[i], ks, vs, cache)
-            fa.decode_attention(qs[i], cache, bts[i], lens, ks, vs, sm, ctx, num_splits=S,
-                                out=out, workspace=ws)
+            dl.run_layer(i)
+
+    def decode_launches():
+        for i in range(layers):
+            dl.run_layer(i, write=False)
 
     for _ in range(args.warmup):
         step()
-    stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
+    e0.record()
     for _ in range(args.steps):
         step()
-    e1.record(stream)
+    e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = e0.elapsed_time(e1) / args.steps
     log(f"step: {ms_step:.4f} ms (events), wall {wall / args.steps * 1e3:.4f} ms")
+    # the dominant kernel alone: the same steps' decode launches back to back
+    # (HIP events around the region; per-launch event pairs would add their
+    # own marker time to every launch)
+    e0.record()
+    for _ in range(args.steps):
+        decode_launches()
+    e1.record()
+    torch.cuda.synchronize()
+    n_launch = args.steps * layers
+    dec_ms = e0.elapsed_time(e1) / n_launch
 
-    step_bytes = layers * (decode_bytes(B, Hq, Hkv, D, ctx, 1) +
-                           cache_write_bytes(B, Hkv, D, 4, 1))
+    step_bytes = layers * (dl.bytes_per_layer + dl.write_bytes)
     value = step_bytes / (ms_step * 1e-3) / 1e9
-
-    # dominant kernel alone: the decode launch (one kernel per call)
-    dec_ms, _ = time_decode(fa, torch, cache, tables, ks, vs, qs[0], ctx, D,
-                            reps=max(args.steps, 5), splits=S)
-    per_launch = decode_bytes(B, Hq, Hkv, D, ctx, 1)
+    per_launch = dl.bytes_per_layer
     achieved = per_launch / (dec_ms * 1e-3) / 1e9
     log(f"decode kernel: {dec_ms * 1e3:.2f} us/launch -> {achieved:.0f} GB/s "
-        f"({achieved / HBM_PEAK_GBS * 100:.1f}% of peak), splits={S}")
-    del cache
-    torch.cuda.empty_cache()
+        f"({achieved / HBM_PEAK_GBS * 100:.1f}% of peak), splits={dl.S}")
+    dl.free()
+    traffic = measured_traffic()
 
     result = {
         "metric": "FP8 decode KV GB/s (% of HBM peak) + ms/ctx-token slope vs BF16 cache",
@@ -364,30 +556,36 @@ def main():
         "dtype": "e4m3 cache, f32 math",
         "data": "synthetic: N(0,1) K/V with 1% outlier channels x20, absmax/448 per-KV-head "
                 "scales, device RNG",
-        "config": {"workload": "Llama-3.1-8B-shaped FP8 decode layer x32 distinct layers",
+        "config": {"workload": "Llama-3.1-8B-shaped FP8 decode step, 32 distinct layers",
                    "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
-                   "block_size": 16, "context": ctx, "layers": layers, "splits": S},
+                   "block_size": 16, "context": ctx, "layers": layers, "splits": dl.S},
         "pct_hbm_peak": round(value / HBM_PEAK_GBS * 100, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None,
-                     "kernel": f"decode_split_kernel<128,4,fp8,4> ({per_launch} algorithmic "
-                               f"bytes/launch, {dec_ms * 1e3:.3f} us avg over "
-                               f"{max(args.steps, 5) * layers} launches)"},
+                     "traffic": None if traffic is None else round(traffic),
+                     "kernel": f"decode_split_kernel, head_dim 128, 4 q heads per KV head, "
+                               f"e4m3 cache: {per_launch} algorithmic bytes/launch, "
+                               f"{dec_ms * 1e3:.3f} us average over {n_launch} "
+                               f"back-to-back launches (the timed steps' decode calls)"},
     }
-    if not args.quick and not args.no_slope:
+    if args.copy_calibration:
+        copy_calibration(fa, torch)
+    if not args.quick:
+        log("streaming-read yardstick")
+        sr = measure_stream_read(fa, torch, per_launch)
+        sr["decode_frac_of_stream_read"] = round(achieved / sr["gbs"], 4)
+        result["stream_read"] = sr
         log("slope: FP8 vs BF16 cache, same kernel")
-        result["slope"] = measure_slope(fa, torch, Hq, Hkv, D, [1024, 8192, 32768, 131072],
-                                        min_pool_bytes=1.1e9, reps=3)
-    if not args.quick and not args.no_prefill:
-        try:
-            result["prefill"] = [measure_prefill(fa, torch, accum_mode=1),
-                                 measure_prefill(fa, torch, accum_mode=0)]
-        except fa.Fa8Error as e:
-            result["prefill"] = f"not measured: {e}"
-    if not args.quick and not args.no_cpu:
-        log("cpu baseline: oracle decode")
-        result["cpu_baseline"] = cpu_baseline(Hq, Hkv, D, ctx)
+        result["slope"] = measure_slope(fa, torch, Hq, Hkv, D, [1024, 8192, 32768, 131072])
+        log("loaded decode")
+        result["loaded"] = measure_loaded(fa, torch)
+        log("hybrid")
+        result["hybrid"] = measure_hybrid(fa, torch)
+        log("head_dim 256")
+        result["hd256"] = measure_hd256(fa, torch)
+        if not args.no_cpu:
+            log("cpu baseline: oracle decode")
+            result["cpu_baseline"] = cpu_baseline(Hq, Hkv, D, ctx)
     print(json.dumps(result), flush=True)
 
 

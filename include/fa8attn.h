@@ -185,6 +185,24 @@ fa8_status fa8_prefill_attention(const void* q, const int32_t* cu_q_lens,
                                  float sm_scale, int32_t window,
                                  int32_t accum_mode, float* out, void* stream);
 
+/*
+ * Bandwidth yardsticks (not part of attention).  Decode is a streaming
+ * reader of the cache, so its HBM rate is also reported against what a plain
+ * streaming read achieves on the same device; the copy is a kernel of known
+ * traffic (reads `bytes`, writes `bytes`) for calibrating hardware byte
+ * counters.
+ *
+ *   fa8_stream_read  reads src[0 .. bytes) once with 16-byte loads; `sink`
+ *                    (device, 4 bytes) is written only for one improbable
+ *                    xor of the data, so the loads cannot be dropped.
+ *   fa8_stream_copy  dst[0 .. bytes) = src[0 .. bytes); the ranges must not
+ *                    overlap.
+ * bytes must be a multiple of 16 (FA8_EINVAL otherwise); pointers 16-byte
+ * aligned device memory; asynchronous on `stream`.
+ */
+fa8_status fa8_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+fa8_status fa8_stream_copy(void* dst, const void* src, size_t bytes, void* stream);
+
 /* Static English name of a status code. */
 const char* fa8_status_string(int32_t status);
 
