@@ -182,8 +182,7 @@ fa8_status fa8_decode_attention(const void* q, int32_t batch, int32_t num_q_head
   p.seq_lens = seq_lens;
   p.k_scale = k_scale;
   p.v_scale = v_scale;
-  fa8::decode_workspace_carve(workspace, batch, num_q_heads, head_dim, S, &p.ws_count,
-                              &p.ws_o, &p.ws_m, &p.ws_l);
+  fa8::decode_workspace_carve(workspace, batch, num_q_heads, head_dim, S, p);
   p.out = out;
   p.batch = batch;
   p.num_q_heads = num_q_heads;
@@ -191,6 +190,8 @@ fa8_status fa8_decode_attention(const void* q, int32_t batch, int32_t num_q_head
   p.head_dim = head_dim;
   p.max_blocks = max_blocks_per_seq;
   p.num_splits = S;
+  p.num_groups = fa8::decode_num_groups(S);
+  p.group_size = p.num_groups == 1 ? S : fa8::kDecodeFan;
   const int pages = decode_pages_max(max_seq_len, window);
   p.pages_per_split = pages > 0 ? (pages + S - 1) / S : 1;
   p.window = window > 0 ? window : 0;

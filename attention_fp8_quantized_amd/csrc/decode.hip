@@ -1,81 +1,61 @@
 // Split-KV decode over the paged FP8 / BF16 cache, with the cross-split
-// log-sum-exp combine fused into the same launch.
+// log-sum-exp merge fused into the same launch.
 //
-// [BLOG] "Performance benchmarks / Single-request benchmark": decode time is
-// the per-token KV read, the FP8 cache is read natively and the online
-// softmax is rescaled as the kernel goes.  [EXPLAINER] "Memory reduction is
-// not speed": dequantisation happens inside the attention kernel, in
-// registers, not as a separate pass back to high precision.
+// [BLOG] "性能 Benchmark / 单请求 Benchmark" (single-request benchmark):
+// decode time is the per-token read of the cache, which the FP8 cache halves;
+// the kernel keeps an online-softmax state that it rescales as it goes.
+// [EXPLAINER] "FP8は値とscaleを組み合わせる": a stored value is a code and a
+// scale; the codes are widened in registers, the scales are folded into the
+// score multiplier (k_scale) and the final merge (v_scale).
 //
-// Work decomposition: one workgroup of NW waves per (split, KV head [x head
-// group], sequence).
-//   * The visible pages of a sequence are cut into `num_splits` contiguous
-//     ranges; the waves of a workgroup take the pages of its range
-//     round-robin.  Each wave reads its block ids once (one lane per page)
-//     and keeps two pages in flight in a 3-deep register ring while it
-//     processes the third, so the block-table lookup never sits on the
-//     load path.
-//   * A page-head is 16 rows of D elements: 16*D*elem contiguous bytes for K
-//     and again for V.  A lane loads CB-byte chunks (16 bytes; 8 for e4m3
-//     with D = 64): LPT = D*elem/CB consecutive lanes cover a row, one
-//     wave-wide load covers TPW = 64/LPT consecutive rows, so every load
-//     instruction reads one contiguous span.  Each lane ends up with RPL
-//     rows of the page (same columns).
-//   * q . k: lanes of a row hold the same column range of q for the GW query
-//     heads that share the KV head (GQA).  e4m3 codes convert exactly to bf16
-//     pairs (one instruction per pair) and feed v_dot2_f32_bf16 with the bf16
-//     query (also exact); bf16 cache rows feed it directly.  The LPT partial
-//     sums are added across lanes with DPP.
-//   * online softmax in the log2 domain; each row slot (LPT lanes) keeps its
-//     own running max m, sum l and fp32 output columns, so nothing is
-//     exchanged between slots inside the loop.  Full pages take a branch
-//     without masking; the pages at the window start / sequence end mask.
-//   * p . v: e4m3 -- two rows of the same lane form a token pair; their codes
-//     are interleaved with v_perm_b32, converted to f16 pairs (exact) and
-//     multiplied with the pair of probabilities rounded to f16 by
-//     v_dot2_f32_f16 (fp32 accumulation).  bf16 -- rows convert to fp32 and
-//     use fp32 FMAs.
-//   * slots merge with shuffles, waves through LDS; each workgroup writes one
-//     unnormalised partial (o, m, l) per query head.  The workgroup that
-//     finishes last for its (sequence, head group) merges the splits:
-//        out = v_scale * sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-// Scales are folded: k_scale into the score multiplier, v_scale into the
-// combine.  Empty splits carry m = -inf and weight 0; an all-empty row is 0.
-
-#include <type_traits>
+// Work decomposition: one workgroup of NW waves per (split, KV head,
+// sequence).  The visible pages of a sequence are cut into `num_splits`
+// contiguous ranges; the waves of a workgroup take the pages of their range
+// round-robin, one page (16 keys) at a time, keeping PD pages in flight in a
+// register ring.  The G query heads that share the KV head are handled
+// together: per page the work is a (16 keys x D) by (D x G) product and its
+// (G x 16) by (16 x D) counterpart, done on the matrix cores:
+//
+//   * loads: lane (r, g) (r = lane % 16, g = lane / 16) reads 16-byte pieces
+//     of key row r at byte offsets 64*hh + 16*g, so each load instruction
+//     covers the first / next 64 bytes of all 16 rows of the page;
+//   * S^T = K . Q^T on v_mfma_f32_16x16x32_bf16: K codes are widened to bf16
+//     (exact), the bf16 query is the other operand (exact; columns >= G are
+//     zero).  The head dim is split into 32-wide chunks whose 8 elements per
+//     lane group are the ones lane group g loaded; the query chunks follow
+//     the same assignment.  The result leaves lane (n, g) with the scores of
+//     keys 4g..4g+3 for query head n;
+//   * softmax in the log2 domain: page maximum per head across the 4 lane
+//     groups (permlane swaps), lazily moved reference maximum, p = 2^(s - m);
+//   * P . V on v_mfma_f32_16x16x16 (f16 for the e4m3 cache: p rounded to f16,
+//     V widened to f16 exactly; bf16 for the bf16 cache with p split into a
+//     bf16 high and low part, two products): lane (n, g) already holds P for
+//     head n and keys 4g..4g+3, the A operand.  V is written to a small
+//     per-wave LDS slice and read back transposed (ds_read_b64_tr_b8 / _b16)
+//     as the B operand (keys 4g..4g+3 of one column per lane).  The output
+//     tile leaves lane (n, g) with O[head 4g+i][16c + n].
+// The waves' states merge through LDS; each workgroup writes one
+// unnormalised partial (o, m, l) per query head, and the workgroup that
+// arrives last for its (sequence, KV head) merges the splits (in two levels
+// when there are many):
+//   out = v_scale * sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+// Empty splits carry m = -inf and weight 0; an all-empty row is 0.
 
 #include "fa8_device.hpp"
 #include "fa8_internal.hpp"
 
-#ifndef FA8_DECODE_F16_PV
-#define FA8_DECODE_F16_PV 1    // e4m3 p.v: f16 probability pairs + v_dot2_f32_f16
-#endif
-
 namespace fa8 {
 
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr int kMaxSplits = kDecodeMaxSplits;
 // lazy-rescale threshold (log2 units): probabilities stay below 2^8, far
 // inside f16 range, and fp32 sums lose nothing
 constexpr float kLazy = 8.0f;
 
-template <int N>
-struct Chunk {
-  uint32_t w[N];
-};
-
-template <int N>
-__device__ __forceinline__ Chunk<N> load_chunk(const uint8_t* p) {
-  Chunk<N> c;
-  if constexpr (N == 4) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
-    c.w[0] = v.x; c.w[1] = v.y; c.w[2] = v.z; c.w[3] = v.w;
-  } else {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    c.w[0] = v.x; c.w[1] = v.y;
-  }
-  return c;
-}
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2* lds_i32x2_ptr;
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 
 // Workspace traffic between workgroups uses agent-scope atomic loads and
 // stores: they are coherent across the chip's separate L2 caches without a
@@ -87,148 +67,195 @@ __device__ __forceinline__ float ld_agent(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Merge the S split partials of GW query heads (run by the last workgroup):
-//   out = v_scale * sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-// The maxima, the denominators and the first CH partial rows of every output
-// element are requested together, so the merge costs one memory round trip
-// whenever S <= CH * R.
-template <int D, int GW, int NW>
-__device__ __forceinline__ void combine_splits(const DecodeParams& p, int b, int h, int hq0) {
+// Reductions over the 64 lanes of a wave: DPP within each row of 16 lanes
+// (pairs, quads, half-rows, rows), then permlane swaps across the rows.
+__device__ __forceinline__ float cross_rows_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v),
+                                            __builtin_bit_cast(uint32_t, v), false, false);
+  v = fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+  r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v),
+                                       __builtin_bit_cast(uint32_t, v), false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float cross_rows_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v),
+                                            __builtin_bit_cast(uint32_t, v), false, false);
+  v = __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+  r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v),
+                                       __builtin_bit_cast(uint32_t, v), false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp<0x141>(v));   // row_half_mirror
+  v = fmaxf(v, dpp<0x140>(v));   // row_mirror
+  return cross_rows_max(v);
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  return cross_rows_sum(group_sum<16>(v));
+}
+
+// Merge n unnormalised partials (o, m, l) of each of GW query heads, run by
+// one workgroup.  Head g's partial rows are rows r0 .. r0+n-1 of a block of
+// `rows` rows starting at (head g) * rows:
+//   M = max_i m_i,  w_i = 2^(m_i - M),  o = sum_i w_i o_i,  l = sum_i w_i l_i.
+// kFinal: out[g][d] = v_scale * o / l (0 when every partial is empty);
+// otherwise the merged partial (o, M, l) is stored at row `dst_row` of a
+// block of `dst_rows` rows per head.  All partial loads of a batch (up to
+// kInFlight per thread) are issued before any is used, and the first batch
+// is in flight while the maxima are reduced.
+template <int D, int GW, int NW, bool kFinal>
+__device__ __forceinline__ void merge_rows(const float* o_in, const float* m_in,
+                                           const float* l_in, int rows, int r0, int n,
+                                           float* o_dst, float* m_dst, float* l_dst,
+                                           int dst_rows, int dst_row, float vsc) {
   constexpr int NT = 64 * NW;
-  constexpr int COLS = GW * D;                    // output elements
-  constexpr int R = NT >= COLS ? NT / COLS : 1;   // threads per output element
-  constexpr int CH = 16;                          // partial rows per thread per pass
-  __shared__ float s_m[GW][kMaxSplits];
-  __shared__ float s_l[GW][kMaxSplits];
+  constexpr int COLS = GW * D;                        // output elements
+  constexpr int R = NT >= COLS ? NT / COLS : 1;       // threads per output element
+  constexpr int EPT = COLS > NT ? COLS / NT : 1;      // output elements per thread
+  constexpr int kInFlight = 32;
+  constexpr int JB = kInFlight / EPT;                 // partial rows per element per batch
+  constexpr int kMaxRows = kDecodeSingleLevel;
+  static_assert(R * COLS == NT || EPT * NT == COLS, "merge tiling");
+  __shared__ float s_w[GW][kMaxRows];
+  __shared__ float s_l[GW][kMaxRows];
   __shared__ float s_mx[GW];
   __shared__ float s_den[GW];
-  const int S = p.num_splits;
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
-  const size_t base = ((size_t)b * p.num_q_heads + hq0) * S;   // row of (g=0, s=0)
-  // this thread's first output element (the loop below covers the rest)
   const int col0 = t / R;
   const int r = t % R;
-  float ov[CH];
-  if (col0 < COLS) {
-    const float* o = p.ws_o + (base + (size_t)(col0 / D) * S) * D + col0 % D;
+
+  float v[EPT][JB];
+  auto issue = [&](int j0) {
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int sp = r + i * R;
-      ov[i] = sp < S ? ld_agent(o + (size_t)sp * D) : 0.f;
+    for (int e = 0; e < EPT; ++e) {
+      const int col = col0 + e * (NT / R);
+      const float* src = o_in + ((size_t)(col / D) * rows + r0) * D + col % D;
+#pragma unroll
+      for (int j = 0; j < JB; ++j) {
+        const int i = min(j0 + r + j * R, n - 1);   // rows past n repeat row n-1, weight 0
+        v[e][j] = ld_agent(src + (size_t)i * D);
+      }
+    }
+  };
+  // the (head, row) maxima and denominators (at most MLT per thread) are
+  // requested before the first batch of partial rows, so that only they are
+  // waited for here
+  constexpr int MLT = (GW * kMaxRows + NT - 1) / NT;
+  float mv[MLT], lv[MLT];
+#pragma unroll
+  for (int k = 0; k < MLT; ++k) {
+    const int i = t + k * NT;
+    mv[k] = kNegInf;
+    lv[k] = 0.f;
+    if (i < GW * n) {
+      mv[k] = ld_agent(m_in + (size_t)(i / n) * rows + r0 + i % n);
+      lv[k] = ld_agent(l_in + (size_t)(i / n) * rows + r0 + i % n);
     }
   }
-  for (int i = t; i < GW * S; i += NT) {
-    s_m[i / S][i % S] = ld_agent(p.ws_m + base + i);
-    s_l[i / S][i % S] = ld_agent(p.ws_l + base + i);
+  issue(0);
+#pragma unroll
+  for (int k = 0; k < MLT; ++k) {
+    const int i = t + k * NT;
+    if (i < GW * n) {
+      s_w[i / n][i % n] = mv[k];
+      s_l[i / n][i % n] = lv[k];
+    }
   }
   __syncthreads();
-  // per head: M, weights 2^(m_s - M) (in place of m) and the denominator
+  // one wave per head: M, weights 2^(m_i - M) (in place of m) and the
+  // denominator, with in-register wave reductions
   for (int g = wave; g < GW; g += NW) {
-    float M = kNegInf;
-    for (int sp = lane; sp < S; sp += 64) M = fmaxf(M, s_m[g][sp]);
-#pragma unroll
-    for (int x = 1; x < 64; x *= 2) M = fmaxf(M, __shfl_xor(M, x));
-    float den = 0.f;
-    for (int sp = lane; sp < S; sp += 64) {
-      const float ms = s_m[g][sp];
-      const float f = (M > kNegInf && ms > kNegInf) ? fast_exp2(ms - M) : 0.f;
-      s_m[g][sp] = f;
-      den += f * s_l[g][sp];
-    }
-#pragma unroll
-    for (int x = 1; x < 64; x *= 2) den += __shfl_xor(den, x);
+    const float mk = lane < n ? s_w[g][lane] : kNegInf;
+    const float M = wave_max(mk);
+    const float f = (M > kNegInf && mk > kNegInf) ? fast_exp2(mk - M) : 0.f;
+    const float den = wave_sum(lane < n ? f * s_l[g][lane] : 0.f);
+    if (lane < n) s_w[g][lane] = f;
     if (lane == 0) {
       s_mx[g] = M;
       s_den[g] = den;
     }
   }
   __syncthreads();
-  const float vsc = p.fp8 ? p.v_scale[h] : 1.0f;
-  for (int col = col0; col < COLS; col += NT / R) {
+  float acc[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) acc[e] = 0.f;
+  for (int j0 = 0; j0 < n; j0 += JB * R) {
+    if (j0 > 0) issue(j0);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int g = (col0 + e * (NT / R)) / D;
+#pragma unroll
+      for (int j = 0; j < JB; ++j) {
+        const int i = j0 + r + j * R;
+        if (i < n) acc[e] += s_w[g][i] * v[e][j];
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    float a = acc[e];
+    a = group_sum<R>(a);   // the R threads of an element are adjacent lanes
+    const int col = col0 + e * (NT / R);
     const int g = col / D;
     const int d = col % D;
-    const float* o = p.ws_o + (base + (size_t)g * S) * D + d;
-    float acc = 0.f;
-    if (col == col0) {
-#pragma unroll
-      for (int i = 0; i < CH; ++i) {
-        const int sp = r + i * R;
-        if (sp < S) acc += s_m[g][sp] * ov[i];
-      }
-    } else {
-      for (int sp = r; sp < min(S, CH * R); sp += R) acc += s_m[g][sp] * ld_agent(o + (size_t)sp * D);
-    }
-    for (int sp = r + CH * R; sp < S; sp += R) acc += s_m[g][sp] * ld_agent(o + (size_t)sp * D);
-#pragma unroll
-    for (int x = 1; x < R; x *= 2) acc += __shfl_xor(acc, x);
     if (r == 0) {
-      const float res = s_mx[g] > kNegInf ? acc * (vsc / s_den[g]) : 0.f;
-      p.out[((size_t)b * p.num_q_heads + hq0 + g) * D + d] = res;
+      if constexpr (kFinal) {
+        o_dst[(size_t)g * D + d] = s_mx[g] > kNegInf ? a * (vsc / s_den[g]) : 0.f;
+      } else {
+        const size_t row = (size_t)g * dst_rows + dst_row;
+        st_agent(o_dst + row * D + d, a);
+        if (d == 0) {
+          st_agent(m_dst + row, s_mx[g]);
+          st_agent(l_dst + row, s_den[g]);
+        }
+      }
     }
   }
 }
 
-// Values of the lane `x` lanes away (x = 8: DPP rotate within a 16-lane row;
-// 16 / 32: permlane swaps), returned as the pair (value from the lower
-// partner, value from the upper partner) so that a symmetric merge needs no
-// select.  For x = 8 the pair is (own, partner).
-template <int X>
-__device__ __forceinline__ void lane_pair(float v, float& a, float& b) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, v);
-  if constexpr (X == 8) {
-    a = v;
-    b = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, (int)u, 0x128, 0xF, 0xF, false));
-  } else if constexpr (X == 16) {
-    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    a = __builtin_bit_cast(float, (uint32_t)r[0]);
-    b = __builtin_bit_cast(float, (uint32_t)r[1]);
-  } else {
-    static_assert(X == 32, "lane distance");
-    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    a = __builtin_bit_cast(float, (uint32_t)r[0]);
-    b = __builtin_bit_cast(float, (uint32_t)r[1]);
-  }
+
+// 8 e4m3 codes (two dwords) -> 8 bf16 (exact)
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
+  const bf16x2 a = e4m3x2_to_bf16<false>(w0), b = e4m3x2_to_bf16<true>(w0);
+  const bf16x2 c = e4m3x2_to_bf16<false>(w1), d = e4m3x2_to_bf16<true>(w1);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-#ifdef FA8_DECODE_WAVES_PER_EU
-#define FA8_DECODE_OCCUPANCY __attribute__((amdgpu_waves_per_eu(FA8_DECODE_WAVES_PER_EU)))
-#else
-#define FA8_DECODE_OCCUPANCY
-#endif
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast(bf16x8, w); }
 
-template <int D, int GWW, int HG, bool kFp8, int NW, int PD>
-__global__ __launch_bounds__(64 * NW) FA8_DECODE_OCCUPANCY void decode_split_kernel(DecodeParams p) {
-  constexpr int ES = kFp8 ? 1 : 2;                     // bytes per element
-  constexpr int CB = (kFp8 && D == 64) ? 8 : 16;       // bytes per lane chunk
-  constexpr int CW = CB / 4;                           // dwords per chunk
-  constexpr int EPC = CB / ES;                         // elements per chunk
-  constexpr int LPT = D / EPC;                         // lanes per row
-  constexpr int TPW = 64 / LPT;                        // rows per wave-load
-  constexpr int RPL = kBlockSize / TPW;                // rows per lane per page
-  constexpr int ROW_BYTES = D * ES;
-  constexpr int HALF_BYTES = kBlockSize * ROW_BYTES;
-  constexpr int GW = GWW * HG;                         // query heads per workgroup
-  constexpr int NPW = NW / HG;                         // waves sharing one head group
-  static_assert(LPT * TPW == 64 && RPL * TPW == kBlockSize, "tiling");
-  static_assert(!kFp8 || RPL % 2 == 0, "e4m3 p.v pairs rows of a lane");
-  static_assert(NW % HG == 0 && PD >= 2 && PD <= 8, "launch shape");
-  using C = Chunk<CW>;
-  constexpr bool kF16PV = FA8_DECODE_F16_PV != 0;
+// Waves per SIMD the register budget is sized for (without spills): four
+// (two 8-wave workgroups per CU) where a page fits, fewer for the larger
+// pages of the bf16 cache and of head_dim 256.
+template <int D, bool kFp8>
+constexpr int decode_min_waves() {
+  return D == 256 ? 2 : (kFp8 || D == 64) ? 4 : 3;
+}
+
+template <int D, int G, bool kFp8, int NW, int PD>
+__global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFp8>())) void decode_split_kernel(DecodeParams p) {
+  constexpr int ES = kFp8 ? 1 : 2;       // bytes per element
+  constexpr int ROW = D * ES;            // bytes per cached row
+  constexpr int HALF = kBlockSize * ROW; // K (or V) bytes of one page-head
+  constexpr int NL = ROW / 64;           // 16-byte loads per lane per page-half
+  constexpr int NQ = D / 32;             // 32-wide head-dim chunks (QK MFMAs per page)
+  constexpr int NB = D / 16;             // 16-wide output column blocks
+  constexpr int BPS = kFp8 ? 4 : 2;      // column blocks per 64-byte slice
+  constexpr int RS = 64 + 16;            // LDS row stride of the V slice (bytes)
+  static_assert(NL >= 1 && NB == NL * BPS, "tiling");
+  static_assert(G >= 1 && G <= 16, "query heads per KV head");
 
   const int split = blockIdx.x;
-  const int G = p.num_q_heads / p.num_kv_heads;
-  const int groups = G / GW;
-  const int h = blockIdx.y / groups;
-  const int hq0 = h * G + (blockIdx.y % groups) * GW;
+  const int h = blockIdx.y;
   const int b = blockIdx.z;
+  const int hq0 = h * G;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int hg = wave % HG;        // which GWW query heads this wave serves
-  const int pw = wave / HG;        // which pages of the split it reads
-  const int slot = lane / LPT;
-  const int c = lane % LPT;
+  const int n = lane & 15;     // key row (loads, K operand) / head (Q, S, P) / column (V, O)
+  const int g = lane >> 4;     // k-group of the MFMA operands
 
   const int L = p.seq_lens[b];
   const int lo = p.window > 0 ? max(0, L - p.window) : 0;
@@ -237,189 +264,169 @@ __global__ __launch_bounds__(64 * NW) FA8_DECODE_OCCUPANCY void decode_split_ker
   const int pg0 = page_lo + split * p.pages_per_split;
   const int pg1 = min(pg0 + p.pages_per_split, page_hi);
 
-  // q columns c*EPC .. c*EPC+EPC-1 of this wave's query heads, as bf16 pairs
-  const int hqw = hq0 + hg * GWW;
-  uint32_t qw[GWW][EPC / 2];
+  // ---- query operand: chunk q holds, for lane group g, head-dim elements
+  //      e4m3 cache: 64*(q/2) + 16*g + 8*(q%2) + i;  bf16 cache: 32*q + 8*g + i
+  bf16x8 qop[NQ];
 #pragma unroll
-  for (int g = 0; g < GWW; ++g) {
-    const uint4* src = reinterpret_cast<const uint4*>(
-        p.q + ((size_t)b * p.num_q_heads + hqw + g) * D + c * EPC);
-#pragma unroll
-    for (int i = 0; i < EPC / 8; ++i) {
-      const uint4 w = src[i];
-      qw[g][4 * i + 0] = w.x;
-      qw[g][4 * i + 1] = w.y;
-      qw[g][4 * i + 2] = w.z;
-      qw[g][4 * i + 3] = w.w;
-    }
+  for (int q = 0; q < NQ; ++q) {
+    const int d0 = kFp8 ? 64 * (q / 2) + 16 * g + 8 * (q % 2) : 32 * q + 8 * g;
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (n < G) w = *reinterpret_cast<const uint4*>(p.q + ((size_t)b * p.num_q_heads + hq0 + n) * D + d0);
+    qop[q] = as_bf16x8(w);
   }
-  const float qk_scale = p.sm_scale * kLog2e * (kFp8 ? p.k_scale[h] : 1.0f);
+  const float qk = p.sm_scale * kLog2e * (kFp8 ? p.k_scale[h] : 1.0f);
 
-  float m[GWW], l[GWW], o[GWW][EPC];
+  float m = kNegInf;   // reference maximum of head n (equal in the 4 lane groups)
+  float l = 0.f;       // sum of p over this lane's keys, head n
+  f32x4 o[NB];         // O[head 4g+i][16c + n]
 #pragma unroll
-  for (int g = 0; g < GWW; ++g) {
-    m[g] = kNegInf;
-    l[g] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) o[g][e] = 0.f;
-  }
+  for (int c = 0; c < NB; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const uint8_t* head_base = p.cache + (size_t)h * 2 * HALF_BYTES + slot * ROW_BYTES + c * CB;
-  const size_t blk_stride = (size_t)p.num_kv_heads * 2 * HALF_BYTES;
+  // one LDS region: V slices during the loop, the wave merge afterwards
+  constexpr int kSliceBytes = kBlockSize * RS;
+  constexpr int kMergeHeads = (32768 / (NW * D * 4)) < G ? (32768 / (NW * D * 4)) : G;
+  constexpr int kMergeBytes = NW * kMergeHeads * D * 4 + 2 * NW * 16 * 4;
+  constexpr int kLdsBytes = NW * kSliceBytes > kMergeBytes ? NW * kSliceBytes : kMergeBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t s_raw[kLdsBytes];
+  uint8_t* sv = s_raw + wave * kSliceBytes;
+
+  const uint8_t* head_base = p.cache + (size_t)h * 2 * HALF + n * ROW + 16 * g;
+  const size_t blk_stride = (size_t)p.num_kv_heads * 2 * HALF;
   const int32_t* bt = p.block_table + (size_t)b * p.max_blocks;
 
   struct Page {
-    C k[RPL], v[RPL];
+    uint4 k[NL], v[NL];
   };
   auto issue = [&](Page& pg, int blk) {
     const uint8_t* kb = head_base + (size_t)blk * blk_stride;
 #pragma unroll
-    for (int r = 0; r < RPL; ++r) pg.k[r] = load_chunk<CW>(kb + r * TPW * ROW_BYTES);
+    for (int hh = 0; hh < NL; ++hh) pg.k[hh] = *reinterpret_cast<const uint4*>(kb + 64 * hh);
 #pragma unroll
-    for (int r = 0; r < RPL; ++r)
-      pg.v[r] = load_chunk<CW>(kb + HALF_BYTES + r * TPW * ROW_BYTES);
+    for (int hh = 0; hh < NL; ++hh) pg.v[hh] = *reinterpret_cast<const uint4*>(kb + HALF + 64 * hh);
   };
 
-  // One page, straight-line: the pages at the window start and sequence end
-  // differ only in the validity mask (a select), so there is a single path.
   auto run_page = [&](const Page& pg, int page) {
-    // ---- scores s = (q . k) * sm_scale * k_scale * log2(e) ------------------
-    float s[RPL][GWW];
+    // ---- S^T = K . Q^T ------------------------------------------------------
+    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < RPL; ++r) {
-      float part[GWW];
-#pragma unroll
-      for (int w = 0; w < CW; ++w) {
-        if constexpr (kFp8) {
-          const bf16x2 k01 = e4m3x2_to_bf16<false>(pg.k[r].w[w]);
-          const bf16x2 k23 = e4m3x2_to_bf16<true>(pg.k[r].w[w]);
-#pragma unroll
-          for (int g = 0; g < GWW; ++g) {
-            part[g] = dot2_bf16(as_bf16x2(qw[g][2 * w]), k01, w == 0 ? 0.f : part[g]);
-            part[g] = dot2_bf16(as_bf16x2(qw[g][2 * w + 1]), k23, part[g]);
-          }
-        } else {
-#pragma unroll
-          for (int g = 0; g < GWW; ++g)
-            part[g] = dot2_bf16(as_bf16x2(qw[g][w]), as_bf16x2(pg.k[r].w[w]),
-                                w == 0 ? 0.f : part[g]);
-        }
+    for (int q = 0; q < NQ; ++q) {
+      bf16x8 a;
+      if constexpr (kFp8) {
+        const uint4 w = pg.k[q / 2];
+        a = (q % 2 == 0) ? e4m3x8_to_bf16(w.x, w.y) : e4m3x8_to_bf16(w.z, w.w);
+      } else {
+        a = as_bf16x8(pg.k[q]);
       }
-#pragma unroll
-      for (int g = 0; g < GWW; ++g) s[r][g] = group_sum<LPT>(part[g]) * qk_scale;
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[q], s, 0, 0, 0);
     }
-    // only the pages at the window start / sequence end hold invisible rows
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] *= qk;
+    // only the pages at the window start / sequence end hold invisible keys
     if (page * kBlockSize < lo || page * kBlockSize + kBlockSize > L) {
 #pragma unroll
-      for (int r = 0; r < RPL; ++r) {
-        const int tok = page * kBlockSize + slot + r * TPW;
-        const bool valid = tok >= lo && tok < L;
-#pragma unroll
-        for (int g = 0; g < GWW; ++g) s[r][g] = valid ? s[r][g] : kNegInf;
+      for (int i = 0; i < 4; ++i) {
+        const int key = page * kBlockSize + 4 * g + i;
+        s[i] = (key >= lo && key < L) ? s[i] : kNegInf;
       }
     }
-    // ---- reference maximum ---------------------------------------------------
-    // m is the slot's reference point, not necessarily its exact maximum: it
-    // moves (and the state is rescaled) only when a score exceeds it by more
-    // than kLazy (log2 units), so p = 2^(s - m) stays below 2^kLazy and the
-    // rescale is rare.  The result is the same softmax (any reference works).
-    float mref[GWW];
+    // ---- reference maximum -------------------------------------------------
+    // m moves (and the state is rescaled) only when a score exceeds it by more
+    // than kLazy, so p = 2^(s - m) < 2^kLazy and rescales are rare; any
+    // reference gives the same softmax.
+    const float mx = cross_rows_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+    const bool up = mx > m + kLazy;
+    if (__builtin_amdgcn_ballot_w64(up)) {
+      const float m_new = up ? mx : m;
+      const float alpha = m_new == m ? 1.0f : fast_exp2(m - m_new);   // 0 while m = -inf
+      l *= alpha;
+      // output rows are heads 4g+i: their factors live in lanes 4g+i
+      float ar[4];
 #pragma unroll
-    for (int g = 0; g < GWW; ++g) {
-      float mx = s[0][g];
+      for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * g + i);
 #pragma unroll
-      for (int r = 1; r < RPL; ++r) mx = fmaxf(mx, s[r][g]);
-      if (mx > m[g] + kLazy) {
-        const float alpha = fast_exp2(m[g] - mx);  // 0 while m is -inf
-        l[g] *= alpha;
+      for (int c = 0; c < NB; ++c)
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) o[g][e] *= alpha;
-        m[g] = mx;
-      }
-      // while nothing is visible yet (m = -inf) every s is -inf: use 0 as the
-      // reference so that exp2(s - ref) = 0 instead of NaN
-      mref[g] = m[g] > kNegInf ? m[g] : 0.f;
+        for (int i = 0; i < 4; ++i) o[c][i] *= ar[i];
+      m = m_new;
     }
-    // ---- probabilities ---------------------------------------------------------
-    float pr[RPL][GWW];
+    // while nothing is visible yet (m = -inf) every s is -inf: reference 0
+    const float mref = m > kNegInf ? m : 0.f;
+    float pr[4];
 #pragma unroll
-    for (int r = 0; r < RPL; ++r)
+    for (int i = 0; i < 4; ++i) {
+      pr[i] = fast_exp2(s[i] - mref);
+      l += pr[i];
+    }
+    // ---- P . V ---------------------------------------------------------------
+    // V slice hh: bytes [64 hh, 64 hh + 64) of the 16 rows, row-major in LDS
+    if constexpr (kFp8) {
+      const f16x4 pa = {(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
 #pragma unroll
-      for (int g = 0; g < GWW; ++g) {
-        pr[r][g] = fast_exp2(s[r][g] - mref[g]);
-        l[g] += pr[r][g];
-      }
-    // ---- p . v -------------------------------------------------------------
-    if constexpr (kFp8 && kF16PV) {
+      for (int hh = 0; hh < NL; ++hh) {
+        *reinterpret_cast<uint4*>(sv + n * RS + 16 * g) = pg.v[hh];
 #pragma unroll
-      for (int r = 0; r < RPL; r += 2) {
-        f16x2 vp[EPC];
-#pragma unroll
-        for (int w = 0; w < CW; ++w) {
-          // bytes [a0 b0 a1 b1] and [a2 b2 a3 b3] of rows r (a) and r+1 (b)
-          const uint32_t lo2 = __builtin_amdgcn_perm(pg.v[r + 1].w[w], pg.v[r].w[w], 0x05010400u);
-          const uint32_t hi2 = __builtin_amdgcn_perm(pg.v[r + 1].w[w], pg.v[r].w[w], 0x07030602u);
-          vp[4 * w + 0] = e4m3x2_to_f16<false>(lo2);
-          vp[4 * w + 1] = e4m3x2_to_f16<true>(lo2);
-          vp[4 * w + 2] = e4m3x2_to_f16<false>(hi2);
-          vp[4 * w + 3] = e4m3x2_to_f16<true>(hi2);
-        }
-#pragma unroll
-        for (int g = 0; g < GWW; ++g) {
-          const f16x2 pp = {(_Float16)pr[r][g], (_Float16)pr[r + 1][g]};
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) o[g][e] = dot2_f16(vp[e], pp, o[g][e]);
+        for (int cb = 0; cb < BPS; ++cb) {
+          // lanes 2j, 2j+1 of the group address the two 8-byte halves of
+          // row 4g + (j & 3) (rows repeat: the low 4 bytes are used); lane n
+          // receives column 16 cb + n of rows 4g .. 4g+3
+          const int j = n >> 1;
+          const i32x2 t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (lds_i32x2_ptr)(sv + (4 * g + (j & 3)) * RS + 16 * cb + 8 * (n & 1)));
+          const f16x2 v01 = e4m3x2_to_f16<false>((uint32_t)t[0]);
+          const f16x2 v23 = e4m3x2_to_f16<true>((uint32_t)t[0]);
+          const f16x4 vb = {v01[0], v01[1], v23[0], v23[1]};
+          o[hh * BPS + cb] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vb, o[hh * BPS + cb], 0, 0, 0);
         }
       }
     } else {
+      // p = hi + lo, both bf16 (together 16 significant bits)
+      s16x4 ph, pl;
 #pragma unroll
-      for (int r = 0; r < RPL; ++r) {
-        float vf[EPC];
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t hb = bf16_bits(pr[i]);
+        ph[i] = (short)hb;
+        pl[i] = (short)bf16_bits(pr[i] - __uint_as_float(hb << 16));
+      }
 #pragma unroll
-        for (int w = 0; w < CW; ++w) {
-          if constexpr (kFp8) {
-            const f32x2 x01 = e4m3x2_to_f32<false>(pg.v[r].w[w]);
-            const f32x2 x23 = e4m3x2_to_f32<true>(pg.v[r].w[w]);
-            vf[4 * w + 0] = x01.x;
-            vf[4 * w + 1] = x01.y;
-            vf[4 * w + 2] = x23.x;
-            vf[4 * w + 3] = x23.y;
-          } else {
-            vf[2 * w + 0] = bf16_lo(pg.v[r].w[w]);
-            vf[2 * w + 1] = bf16_hi(pg.v[r].w[w]);
-          }
+      for (int hh = 0; hh < NL; ++hh) {
+        *reinterpret_cast<uint4*>(sv + n * RS + 16 * g) = pg.v[hh];
+#pragma unroll
+        for (int cb = 0; cb < BPS; ++cb) {
+          // lane j of the group addresses elements 16 cb + 4 (j & 3) .. +3 of
+          // row 4g + (j >> 2); lane 4a + b receives element b of the pieces
+          // of lanes a, a+4, a+8, a+12: column 16 cb + n of rows 4g .. 4g+3
+          const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4_ptr)(sv + (4 * g + (n >> 2)) * RS + 2 * (16 * cb + 4 * (n & 3))));
+          f32x4 acc = o[hh * BPS + cb];
+          acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vb, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vb, acc, 0, 0, 0);
+          o[hh * BPS + cb] = acc;
         }
-#pragma unroll
-        for (int g = 0; g < GWW; ++g)
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) o[g][e] = fmaf(pr[r][g], vf[e], o[g][e]);
       }
     }
   };
 
-  // This wave's pages: pg0 + pw + NPW*j.  Block ids are fetched 64 at a
-  // time, one per lane, and broadcast with readlane; PD-1 pages are in
-  // flight while one is processed.
-  const int first = pg0 + pw;
-  const int npw = first < pg1 ? (pg1 - first + NPW - 1) / NPW : 0;
+  // This wave's pages: pg0 + wave + NW*j.  Block ids are fetched 64 at a
+  // time, one per lane, and broadcast with readlane.  Steady PD-deep ring:
+  // every buffer is consumed and re-issued in every round, and prefetches
+  // past the end repeat the last page (a cache hit), so every path keeps the
+  // same loads in flight and the compiler waits for exactly the page it is
+  // about to use.
+  const int first = pg0 + wave;
+  const int npw = first < pg1 ? (pg1 - first + NW - 1) / NW : 0;
   for (int jb = 0; jb < npw; jb += 64) {
-    const int n = min(64, npw - jb);
-    const int page_base = first + NPW * jb;
-    const int my_blk = lane < n ? bt[page_base + NPW * lane] : 0;
-    // Steady PD-deep ring: PD-1 pages are in flight while one is processed.
-    // Every buffer is consumed and re-issued in every round, and prefetches
-    // past the end repeat the last page (an L2 hit), so every path keeps the
-    // same loads in flight and the compiler waits for exactly the page it is
-    // about to use.
-    auto blk_of = [&](int j) { return __builtin_amdgcn_readlane(my_blk, min(j, n - 1)); };
+    const int cnt = min(64, npw - jb);
+    const int page_base = first + NW * jb;
+    const int my_blk = lane < cnt ? bt[page_base + NW * lane] : 0;
+    auto blk_of = [&](int j) { return __builtin_amdgcn_readlane(my_blk, min(j, cnt - 1)); };
     Page ring[PD];
 #pragma unroll
     for (int k = 0; k < PD; ++k) issue(ring[k], blk_of(k));
     int j = 0;
-    for (; j + PD <= n; j += PD) {
+    for (; j + PD <= cnt; j += PD) {
 #pragma unroll
       for (int k = 0; k < PD; ++k) {
-        run_page(ring[k], page_base + NPW * (j + k));
+        run_page(ring[k], page_base + NW * (j + k));
         __builtin_amdgcn_sched_barrier(0);   // keep the reissue after the use
         issue(ring[k], blk_of(j + k + PD));
         __builtin_amdgcn_sched_barrier(0);
@@ -427,153 +434,164 @@ __global__ __launch_bounds__(64 * NW) FA8_DECODE_OCCUPANCY void decode_split_ker
     }
 #pragma unroll
     for (int k = 0; k < PD - 1; ++k)
-      if (j + k < n) run_page(ring[k], page_base + NPW * (j + k));
+      if (j + k < cnt) run_page(ring[k], page_base + NW * (j + k));
   }
 
-  // ---- merge the TPW row slots of the wave (lanes with equal c) -------------
-  // Slots sit LPT, 2*LPT, ... lanes apart; each step merges a lane's state
-  // with its partner's (a symmetric merge, so both partners end up equal).
-  auto merge_step = [&](auto xtag) {
-    constexpr int X = decltype(xtag)::value;
-#pragma unroll
-    for (int g = 0; g < GWW; ++g) {
-      float ma, mb, la, lb;
-      lane_pair<X>(m[g], ma, mb);
-      lane_pair<X>(l[g], la, lb);
-      const float M = fmaxf(ma, mb);
-      const float fa = ma > kNegInf ? fast_exp2(ma - M) : 0.f;
-      const float fb = mb > kNegInf ? fast_exp2(mb - M) : 0.f;
-      l[g] = fa * la + fb * lb;
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) {
-        float oa, ob;
-        lane_pair<X>(o[g][e], oa, ob);
-        o[g][e] = fa * oa + fb * ob;
-      }
-      m[g] = M;
-    }
-  };
-  if constexpr (LPT <= 8) merge_step(std::integral_constant<int, 8>{});
-  if constexpr (LPT <= 16) merge_step(std::integral_constant<int, 16>{});
-  if constexpr (LPT <= 32) merge_step(std::integral_constant<int, 32>{});
-
-  // ---- merge the waves of each head group through LDS (one round) ----------
-  __shared__ float s_o[NW][GWW][D];
-  __shared__ float s_m[NW][GWW];
-  __shared__ float s_l[NW][GWW];
-  __shared__ int s_last;
+  // ---- merge the waves through LDS, kMergeHeads query heads per round -------
+  l = cross_rows_sum(l);     // all keys of this wave, head n
+  float* s_o = reinterpret_cast<float*>(s_raw);                  // [NW][kMergeHeads][D]
+  float* s_m = s_o + NW * kMergeHeads * D;                       // [NW][16]
+  float* s_l = s_m + NW * 16;                                    // [NW][16]
   const int S = p.num_splits;
-  if (slot == 0) {
+  __shared__ int s_last;
+  __syncthreads();            // the V slices are dead from here on
+  if (lane < 16) {
+    s_m[wave * 16 + lane] = m;
+    s_l[wave * 16 + lane] = l;
+  }
 #pragma unroll
-    for (int g = 0; g < GWW; ++g) {
+  for (int r0 = 0; r0 < G; r0 += kMergeHeads) {
+    // this wave's rows r0 .. r0 + kMergeHeads - 1
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) s_o[wave][g][c * EPC + e] = o[g][e];
-      if (c == 0) {
-        s_m[wave][g] = m[g];
-        s_l[wave][g] = l[g];
+    for (int c = 0; c < NB; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hd = 4 * g + i - r0;
+        if (hd >= 0 && hd < kMergeHeads && 4 * g + i < G)
+          s_o[(wave * kMergeHeads + hd) * D + 16 * c + n] = o[c][i];
+      }
+    __syncthreads();
+    for (int t = threadIdx.x; t < kMergeHeads * D; t += 64 * NW) {
+      const int hd = t / D;
+      const int d = t % D;
+      const int hq = r0 + hd;
+      if (hq < G) {
+        float M = kNegInf;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w * 16 + hq]);
+        float num = 0.f, den = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const float mw = s_m[w * 16 + hq];
+          const float f = mw > kNegInf ? fast_exp2(mw - M) : 0.f;
+          num += f * s_o[(w * kMergeHeads + hd) * D + d];
+          den += f * s_l[w * 16 + hq];
+        }
+        const size_t row = ((size_t)b * p.num_q_heads + hq0 + hq) * S + split;
+        st_agent(p.ws_o + row * D + d, num);
+        if (d == 0) {
+          st_agent(p.ws_m + row, M);
+          st_agent(p.ws_l + row, den);
+        }
       }
     }
-  }
-  __syncthreads();
-  // element t: head group hgi, local head g, column d; all stores are issued
-  // back to back and waited for once below
-  for (int t = threadIdx.x; t < HG * GWW * D; t += 64 * NW) {
-    const int hgi = t / (GWW * D);
-    const int g = (t / D) % GWW;
-    const int d = t % D;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = hgi; w < NW; w += HG) M = fmaxf(M, s_m[w][g]);
-    float num = 0.f, den = 0.f;
-#pragma unroll
-    for (int w = hgi; w < NW; w += HG) {
-      const float f = s_m[w][g] > kNegInf ? fast_exp2(s_m[w][g] - M) : 0.f;
-      num += f * s_o[w][g][d];
-      den += f * s_l[w][g];
-    }
-    const size_t row = ((size_t)b * p.num_q_heads + hq0 + hgi * GWW + g) * S + split;
-    st_agent(p.ws_o + row * D + d, num);
-    if (d == 0) {
-      st_agent(p.ws_m + row, M);
-      st_agent(p.ws_l + row, den);
-    }
+    if (r0 + kMergeHeads < G) __syncthreads();
   }
 
   // ---- the last workgroup of this (sequence, head group) merges the splits -
   // Each thread waits until its partial stores are performed (they are
-  // coherent agent-scope stores), the workgroup then counts its arrival; the
-  // one that arrives last reads the partials with coherent loads, writes the
-  // output and re-arms the counter for the next call.  No workgroup waits.
+  // coherent agent-scope stores), then the workgroup counts its arrival.  With
+  // one split group the last arrival merges all splits into the output; with
+  // several, the last arrival of each group merges the group into a group
+  // partial and counts at the second level, whose last arrival merges the
+  // group partials.  Each merger re-arms its counter for the next call.  No
+  // workgroup waits for another.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  int* counter = p.ws_count + (size_t)b * gridDim.y + blockIdx.y;
+  const int NG = p.num_groups;
+  const int grp = split / p.group_size;
+  const int gr0 = grp * p.group_size;
+  const int gn = min(p.group_size, S - gr0);
+  const size_t set = (size_t)b * gridDim.y + blockIdx.y;
+  int* counter = p.ws_count + set * NG + grp;
   if (threadIdx.x == 0)
-    s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+    s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gn - 1;
   __syncthreads();
   if (!s_last) return;
-  combine_splits<D, GW, NW>(p, b, h, hq0);
-  if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const size_t head0 = (size_t)b * p.num_q_heads + hq0;   // first query head of the set
+  const float vsc = p.fp8 ? p.v_scale[h] : 1.0f;
+  if (NG == 1) {
+    merge_rows<D, G, NW, true>(p.ws_o + head0 * S * D, p.ws_m + head0 * S, p.ws_l + head0 * S,
+                                S, 0, S, p.out + head0 * D, nullptr, nullptr, 0, 0, vsc);
+    if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  merge_rows<D, G, NW, false>(p.ws_o + head0 * S * D, p.ws_m + head0 * S, p.ws_l + head0 * S,
+                               S, gr0, gn, p.ws_o1 + head0 * NG * D, p.ws_m1 + head0 * NG,
+                               p.ws_l1 + head0 * NG, NG, grp, vsc);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  int* counter2 = p.ws_count2 + set;
+  if (threadIdx.x == 0) {
+    __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = __hip_atomic_fetch_add(counter2, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == NG - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  merge_rows<D, G, NW, true>(p.ws_o1 + head0 * NG * D, p.ws_m1 + head0 * NG,
+                              p.ws_l1 + head0 * NG, NG, 0, NG, p.out + head0 * D, nullptr,
+                              nullptr, 0, 0, vsc);
+  if (threadIdx.x == 0) __hip_atomic_store(counter2, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 static size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
-static size_t decode_workspace_counter_bytes(int batch, int num_q_heads) {
-  // one arrival counter per (sequence, query head) bounds the number of
-  // (sequence, KV head, head group) workgroup sets
-  return align16((size_t)batch * num_q_heads * 4);
-}
-
+// Counter sets are bounded by B * Hq (one per sequence, KV head and head
+// group).
 size_t decode_workspace_bytes(int batch, int num_q_heads, int head_dim, int splits) {
-  const size_t rows = (size_t)batch * num_q_heads * splits;
-  return decode_workspace_counter_bytes(batch, num_q_heads) + align16(rows * head_dim * 4) +
-         2 * align16(rows * 4);
+  const size_t heads = (size_t)batch * num_q_heads;
+  const int ng = decode_num_groups(splits);
+  size_t n = align16(heads * (ng + 1) * 4);
+  n += align16(heads * splits * head_dim * 4) + 2 * align16(heads * splits * 4);
+  if (ng > 1) n += align16(heads * ng * head_dim * 4) + 2 * align16(heads * ng * 4);
+  return n;
 }
 
 void decode_workspace_carve(void* ws, int batch, int num_q_heads, int head_dim, int splits,
-                            int** count, float** o, float** m, float** l) {
-  const size_t rows = (size_t)batch * num_q_heads * splits;
-  char* base = reinterpret_cast<char*>(ws);
-  *count = reinterpret_cast<int*>(base);
-  base += decode_workspace_counter_bytes(batch, num_q_heads);
-  *o = reinterpret_cast<float*>(base);
-  *m = reinterpret_cast<float*>(base + align16(rows * head_dim * 4));
-  *l = reinterpret_cast<float*>(base + align16(rows * head_dim * 4) + align16(rows * 4));
+                            DecodeParams& p) {
+  const size_t heads = (size_t)batch * num_q_heads;
+  const int ng = decode_num_groups(splits);
+  char* at = reinterpret_cast<char*>(ws);
+  p.ws_count = reinterpret_cast<int*>(at);
+  p.ws_count2 = p.ws_count + heads * ng;
+  at += align16(heads * (ng + 1) * 4);
+  p.ws_o = reinterpret_cast<float*>(at);
+  at += align16(heads * splits * head_dim * 4);
+  p.ws_m = reinterpret_cast<float*>(at);
+  at += align16(heads * splits * 4);
+  p.ws_l = reinterpret_cast<float*>(at);
+  at += align16(heads * splits * 4);
+  p.ws_o1 = p.ws_m1 = p.ws_l1 = nullptr;
+  if (ng > 1) {
+    p.ws_o1 = reinterpret_cast<float*>(at);
+    at += align16(heads * ng * head_dim * 4);
+    p.ws_m1 = reinterpret_cast<float*>(at);
+    at += align16(heads * ng * 4);
+    p.ws_l1 = reinterpret_cast<float*>(at);
+  }
 }
 
 #ifndef FA8_DECODE_PIPE
-#define FA8_DECODE_PIPE 2      // e4m3 cache: pages held per wave (in flight + processed)
-#endif
-#ifndef FA8_DECODE_PIPE_BF16
-#define FA8_DECODE_PIPE_BF16 2 // bf16 cache (pages are twice as large)
-#endif
-#ifndef FA8_DECODE_MAX_GWW
-#define FA8_DECODE_MAX_GWW 4   // query heads per wave for head_dim 64 / 128
+#define FA8_DECODE_PIPE 2      // pages in flight per wave
 #endif
 
-// Launch shape per (D, cache type): query heads per wave (GWW), waves per
-// workgroup (NW).  Heads of one KV head beyond GWW go to other waves of the
-// same workgroup (head groups), which read the same pages (L2 hits).
-template <int D, bool kFp8, int GWW, int HG>
+template <int D, int G, bool kFp8>
 static void launch_shape(const DecodeParams& p, dim3 grid, hipStream_t stream) {
   constexpr int NW = kDecodeWaves;
-  constexpr int PD = kFp8 ? FA8_DECODE_PIPE : FA8_DECODE_PIPE_BF16;
-  hipLaunchKernelGGL((decode_split_kernel<D, GWW, HG, kFp8, NW, PD>), grid,
-                     dim3(64 * NW), 0, stream, p);
+  hipLaunchKernelGGL((decode_split_kernel<D, G, kFp8, NW, FA8_DECODE_PIPE>), grid, dim3(64 * NW),
+                     0, stream, p);
 }
 
 template <int D, bool kFp8>
 static hipError_t launch_decode_d(const DecodeParams& p, hipStream_t stream) {
-  // at most 4 query heads per wave (2 for head_dim 256) keeps registers
-  // below the spill point; at most 8 heads per workgroup
-  constexpr int kMaxGWW = D == 256 ? 2 : FA8_DECODE_MAX_GWW;
   const int G = p.num_q_heads / p.num_kv_heads;
-  const int GW = G > 8 ? 8 : G;
-  dim3 grid(p.num_splits, p.num_kv_heads * (G / GW), p.batch);
-  switch (GW) {
-    case 1: launch_shape<D, kFp8, 1, 1>(p, grid, stream); break;
-    case 2: launch_shape<D, kFp8, 2, 1>(p, grid, stream); break;
-    case 4: launch_shape<D, kFp8, (4 > kMaxGWW ? kMaxGWW : 4), (4 > kMaxGWW ? 4 / kMaxGWW : 1)>(p, grid, stream); break;
-    case 8: launch_shape<D, kFp8, kMaxGWW, 8 / kMaxGWW>(p, grid, stream); break;
+  const dim3 grid(p.num_splits, p.num_kv_heads, p.batch);
+  switch (G) {
+    case 1: launch_shape<D, 1, kFp8>(p, grid, stream); break;
+    case 2: launch_shape<D, 2, kFp8>(p, grid, stream); break;
+    case 4: launch_shape<D, 4, kFp8>(p, grid, stream); break;
+    case 8: launch_shape<D, 8, kFp8>(p, grid, stream); break;
+    case 16: launch_shape<D, 16, kFp8>(p, grid, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -21,28 +21,44 @@ struct DecodeParams {
   const int32_t* seq_lens;    // [B]
   const float* k_scale;       // [Hkv]
   const float* v_scale;       // [Hkv]
-  int* ws_count;              // arrival counters, zero between calls
+  int* ws_count;              // group arrival counters [B][Hq][NG], zero between calls
+  int* ws_count2;             // second-level counters [B][Hq], zero between calls
   float* ws_o;                // [B][Hq][S][D]
   float* ws_m;                // [B][Hq][S]  (log2 domain)
   float* ws_l;                // [B][Hq][S]
+  float* ws_o1;               // [B][Hq][NG][D] group partials (NG > 1 only)
+  float* ws_m1;               // [B][Hq][NG]
+  float* ws_l1;               // [B][Hq][NG]
   float* out;                 // [B][Hq][D]
   int batch, num_q_heads, num_kv_heads, head_dim, max_blocks;
   int num_splits, pages_per_split, window, fp8;
+  int num_groups, group_size; // split groups merged first (1 group: single level)
   float sm_scale;
 };
 
-// Decode workspace layout for `splits` splits (each array 16-byte aligned):
-// int32 arrival counters [B][Hq] (zero before the first call; every call
-// leaves them zero), then fp32 o_part [B][Hq][S][D], m [B][Hq][S] and
-// l [B][Hq][S].
+// Splits are merged in one level when there are at most kDecodeSingleLevel
+// of them; beyond that, groups of kDecodeFan splits are merged first (by
+// the last workgroup of each group) and the group results then (by the
+// last group merger), so no workgroup merges more than 64 partials.
 constexpr int kDecodeMaxSplits = 256;
+constexpr int kDecodeSingleLevel = 64;
+constexpr int kDecodeFan = 16;
+inline int decode_num_groups(int splits) {
+  return splits <= kDecodeSingleLevel ? 1 : (splits + kDecodeFan - 1) / kDecodeFan;
+}
+
+// Decode workspace layout for `splits` splits (each array 16-byte aligned):
+// int32 arrival counters [B][Hq][NG] and [B][Hq] (zero before the first
+// call; every call leaves them zero), fp32 o_part [B][Hq][S][D], m and l
+// [B][Hq][S], and for NG > 1 the group partials o [B][Hq][NG][D], m, l
+// [B][Hq][NG].
 #ifndef FA8_DECODE_WAVES
 #define FA8_DECODE_WAVES 8
 #endif
 constexpr int kDecodeWaves = FA8_DECODE_WAVES;   // waves per decode workgroup
 size_t decode_workspace_bytes(int batch, int num_q_heads, int head_dim, int splits);
 void decode_workspace_carve(void* ws, int batch, int num_q_heads, int head_dim, int splits,
-                            int** count, float** o, float** m, float** l);
+                            DecodeParams& p);
 
 hipError_t launch_decode(const DecodeParams& p, bool fp8_cache, hipStream_t stream);
 

@@ -50,12 +50,27 @@ def test_kv_tile_contract(lib):
     assert lib.fa8_prefill_kv_tile(96) == 0
 
 
+def _ws_expected(B, Hq, D, S):
+    """Documented layout: int32 counters B*Hq*(NG+1), fp32 o_part B*Hq*S*D,
+    m and l B*Hq*S, and for S > 64 the group partials B*Hq*NG*(D+2) with
+    NG = ceil(S/16); every array starts on a 16-byte boundary."""
+    a16 = lambda x: (x + 15) // 16 * 16  # noqa: E731
+    ng = 1 if S <= 64 else -(-S // 16)
+    n = a16(B * Hq * (ng + 1) * 4) + a16(B * Hq * S * D * 4) + 2 * a16(B * Hq * S * 4)
+    if ng > 1:
+        n += a16(B * Hq * ng * D * 4) + 2 * a16(B * Hq * ng * 4)
+    return n
+
+
 def test_workspace_size(lib):
-    # counters B*Hq int32, o_part B*Hq*S*D fp32, m and l B*Hq*S fp32 each;
-    # every array starts on a 16-byte boundary
     assert lib.fa8_decode_workspace_bytes(1, 32, 128, 64) == \
-        32 * 4 + 32 * 64 * 128 * 4 + 2 * 32 * 64 * 4
+        32 * 2 * 4 + 32 * 64 * 128 * 4 + 2 * 32 * 64 * 4
     assert lib.fa8_decode_workspace_bytes(1, 1, 64, 1) == 16 + 256 + 16 + 16
+    # 256 splits: 16 groups of 16
+    assert lib.fa8_decode_workspace_bytes(1, 8, 256, 256) == \
+        8 * 17 * 4 + 8 * 256 * 256 * 4 + 2 * 8 * 256 * 4 + 8 * 16 * 256 * 4 + 2 * 8 * 16 * 4
+    for B, Hq, D, S in [(3, 5, 64, 65), (2, 7, 128, 100), (1, 1, 256, 250), (8, 64, 64, 2)]:
+        assert lib.fa8_decode_workspace_bytes(B, Hq, D, S) == _ws_expected(B, Hq, D, S)
     assert lib.fa8_decode_workspace_bytes(0, 1, 64, 1) == 0
 
 
