@@ -13,11 +13,12 @@
 // and width are part of the numeric contract, see fa8_prefill_kv_tile).
 //
 // Per KV tile:
-//   * the tile's K and V rows (8 pages) are copied into LDS with 16-byte
-//     loads; K codes are widened to bf16 on the way (exact: bf16 holds every
-//     e4m3 value), V stays e4m3;
-//   * S^T = K . Q^T on v_mfma_f32_16x16x32_bf16: the A operand is 8 K values
-//     of one key row per lane, the B operand the e4m3-quantised query
+//   * the tile's K and V rows (8 pages, e4m3) are copied into LDS with
+//     16-byte loads, whole rows per load instruction; the block ids of the
+//     next tile are fetched during the current one;
+//   * S^T = K . Q^T on v_mfma_f32_16x16x32_bf16: the A operand is 8 K codes
+//     of one key row per lane, widened to bf16 after the LDS read (exact:
+//     bf16 holds every e4m3 value), the B operand the e4m3-quantised query
 //     (decoded to bf16, exact; held in registers for the whole kernel).  The
 //     products are exactly the e4m3 x e4m3 products; the bf16 MFMA sums
 //     them in fp32.  (The FP8 MFMA of this chip sums its 128 products with
@@ -85,14 +86,14 @@ __device__ __forceinline__ float group4_sum(float v) {
 }
 
 template <int D>
-__global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(PrefillParams p) {
   constexpr int KQ = D / 32;               // 32-wide chunks of the head dim (bf16 MFMA K)
-  constexpr int RSK = 2 * D + 16;          // LDS row stride of bf16 K (bytes)
-  constexpr int RSV = D + 16;              // LDS row stride of e4m3 V (bytes)
+  constexpr int RS = D + 16;               // LDS row stride of the e4m3 K and V rows (bytes)
   constexpr int DB = D / 16;               // 16-wide output column blocks
-  __shared__ __attribute__((aligned(16))) uint8_t s_kv[kTileN * (RSK + RSV)];
+  __shared__ __attribute__((aligned(16))) uint8_t s_kv[2 * kTileN * RS];
+  __shared__ int s_bt[2][kTileN / kBlockSize];   // block ids of this tile and the next
   uint8_t* s_k = s_kv;
-  uint8_t* s_v = s_kv + kTileN * RSK;
+  uint8_t* s_v = s_kv + kTileN * RS;
 
   const int hq = blockIdx.y;
   const int b = blockIdx.z;
@@ -100,7 +101,9 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
   const int h = hq / G;
   const int qs = p.cu_q_lens[b];
   const int T = p.cu_q_lens[b + 1] - qs;
-  const int q0 = blockIdx.x * kBlockM;
+  // longest causal blocks first: block x of the grid takes query block
+  // (gridDim.x - 1 - x)
+  const int q0 = (gridDim.x - 1 - blockIdx.x) * kBlockM;
   if (q0 >= T) return;
   const int L = p.seq_lens[b];
   const int P0 = L - T;                    // position of the chunk's first query
@@ -155,67 +158,101 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // block ids of the first tile (pages past the sequence end: -1)
+  constexpr int PPT = kTileN / kBlockSize;          // pages per tile
+  if (threadIdx.x < PPT) {
+    const int page = t_lo * PPT + threadIdx.x;
+    s_bt[t_lo & 1][threadIdx.x] = page < n_pages ? bt[page] : -1;
+  }
   for (int t = t_lo; t <= t_hi; ++t) {
-    // ---- stage the tile's K (as bf16) and V (e4m3) rows in LDS ---------------
-    // zeros past the end of the sequence
+    // ---- stage the tile's K and V rows (e4m3) in LDS ----------------------------
+    // chunk c of the tile: page-half c / (16*D/16) (K pages, then V pages),
+    // 16 bytes each; consecutive threads take consecutive chunks of a
+    // page-half, so every load instruction reads whole rows.  Zeros past the
+    // end of the sequence.
     __syncthreads();
-    constexpr int C16 = D / 16;                       // 16-byte chunks per cached row
-    for (int ci = threadIdx.x; ci < 2 * kTileN * C16; ci += 64 * kWaves) {
-      const int kv = ci / (kTileN * C16);
-      const int rem = ci % (kTileN * C16);
-      const int key = rem / C16;
-      const int c16 = rem % C16;
-      const int page = (t * kTileN + key) / kBlockSize;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (page < n_pages) {
-        const uint8_t* src = p.cache + (size_t)bt[page] * blk_stride + head_off +
-                             (size_t)kv * kBlockSize * D + (key % kBlockSize) * D + c16 * 16;
-        val = *reinterpret_cast<const uint4*>(src);
-      }
-      if (kv == 0) {
-        const uint32_t w[4] = {val.x, val.y, val.z, val.w};
-        uint32_t o8[8];
+    constexpr int CPH = kBlockSize * D / 16;          // chunks per page-half
+    constexpr int CPT = 2 * PPT * CPH;                // chunks per tile
+    static_assert(CPT % (64 * kWaves) == 0, "staging tiling");
+    constexpr int NCH = CPT / (64 * kWaves);          // chunks per thread
+    constexpr int BAT = NCH < 8 ? NCH : 8;            // chunks in flight per batch
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          o8[2 * q4] = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16<false>(w[q4]));
-          o8[2 * q4 + 1] = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16<true>(w[q4]));
-        }
-        uint4* dst = reinterpret_cast<uint4*>(s_k + key * RSK + c16 * 32);
-        dst[0] = make_uint4(o8[0], o8[1], o8[2], o8[3]);
-        dst[1] = make_uint4(o8[4], o8[5], o8[6], o8[7]);
-      } else {
-        *reinterpret_cast<uint4*>(s_v + key * RSV + c16 * 16) = val;
+    for (int k0 = 0; k0 < NCH; k0 += BAT) {
+      uint4 val[BAT];
+#pragma unroll
+      for (int k = 0; k < BAT; ++k) {
+        const int c = threadIdx.x + (k0 + k) * 64 * kWaves;
+        const int ph = c / CPH;                        // 0..PPT-1: K of page ph; PPT..: V
+        const int blk = s_bt[t & 1][ph % PPT];
+        val[k] = make_uint4(0, 0, 0, 0);
+        if (blk >= 0)
+          val[k] = *reinterpret_cast<const uint4*>(p.cache + (size_t)blk * blk_stride + head_off +
+                                                   (size_t)(ph / PPT) * kBlockSize * D +
+                                                   (c % CPH) * 16);
       }
+#pragma unroll
+      for (int k = 0; k < BAT; ++k) {
+        const int c = threadIdx.x + (k0 + k) * 64 * kWaves;
+        const int ph = c / CPH;
+        const int within = c % CPH;
+        const int row = (ph % PPT) * kBlockSize + within / (D / 16);
+        *reinterpret_cast<uint4*>((ph / PPT ? s_v : s_k) + row * RS + (within % (D / 16)) * 16) =
+            val[k];
+      }
+    }
+    // the next tile's block ids, requested now and stored after this tile's
+    // compute (its slot is not read during this tile)
+    int next_blk = -1;
+    if (threadIdx.x < PPT && t < t_hi) {
+      const int page = (t + 1) * PPT + threadIdx.x;
+      next_blk = page < n_pages ? bt[page] : -1;
     }
     __syncthreads();
 
     // ---- S^T = K . Q^T : 8 blocks of 16 keys -----------------------------------
+    // the A operand: 8 K codes of key 16 mb + n, columns 32 kq + 8 g, widened
+    // to bf16 (exact)
     f32x4 s[8];
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kq = 0; kq < KQ; ++kq) {
-        const uint4 a = *reinterpret_cast<const uint4*>(s_k + (16 * mb + n) * RSK +
-                                                         (kq * 32 + g * 8) * 2);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), qb[kq],
-                                                       acc, 0, 0, 0);
+        const uint2 a = *reinterpret_cast<const uint2*>(s_k + (16 * mb + n) * RS + kq * 32 + g * 8);
+        const bf16x2 a0 = e4m3x2_to_bf16<false>(a.x), a1 = e4m3x2_to_bf16<true>(a.x);
+        const bf16x2 a2 = e4m3x2_to_bf16<false>(a.y), a3 = e4m3x2_to_bf16<true>(a.y);
+        const bf16x8 av = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[kq], acc, 0, 0, 0);
       }
       s[mb] = acc;
     }
 
     // ---- scale, mask, tile maximum ------------------------------------------
+    // tiles wholly visible to every row of the block skip the mask
+    const int k_first = t * kTileN, k_last = k_first + kTileN - 1;
+    const bool full = k_last <= P0 + q0 && q0 + kBlockM <= T &&
+                      (p.window <= 0 || P0 + rmax - k_first < p.window);
     float tmax = kNegInfP;
+    if (full) {
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
+      for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = t * kTileN + 16 * mb + 4 * g + i;
-        const bool vis = row_ok && key <= pos && (p.window <= 0 || pos - key < p.window);
-        const float v = vis ? s[mb][i] * qk : kNegInfP;
-        s[mb][i] = v;
-        tmax = fmaxf(tmax, v);
-      }
+        for (int i = 0; i < 4; ++i) {
+          s[mb][i] *= qk;
+          tmax = fmaxf(tmax, s[mb][i]);
+        }
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = k_first + 16 * mb + 4 * g + i;
+          const bool vis = row_ok && key <= pos && (p.window <= 0 || pos - key < p.window);
+          const float v = vis ? s[mb][i] * qk : kNegInfP;
+          s[mb][i] = v;
+          tmax = fmaxf(tmax, v);
+        }
+    }
     tmax = group4_max(tmax);
     const float m_new = fmaxf(m_run, tmax);
     const float ref = m_new > kNegInfP ? m_new : 0.f;
@@ -255,7 +292,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
         // the two 8-byte halves of the block's 16 columns
         const int j = n >> 1;
         const int key = 32 * r + 16 * (j >> 2) + 4 * g + (j & 3);
-        const i32x2 v2 = lds_read_tr8(s_v + key * RSV + 16 * db + (n & 1) * 8);
+        const i32x2 v2 = lds_read_tr8(s_v + key * RS + 16 * db + (n & 1) * 8);
         vb[2 * r] = v2[0];
         vb[2 * r + 1] = v2[1];
       }
@@ -270,6 +307,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
         o[db] = mfma_fp8(pa, vb, c);
       }
     }
+    if (threadIdx.x < PPT && t < t_hi) s_bt[(t + 1) & 1][threadIdx.x] = next_blk;
   }
 
   // ---- epilogue: out = O * v_scale / l ---------------------------------------
