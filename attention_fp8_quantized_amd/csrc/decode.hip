@@ -322,11 +322,24 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFp8>())) void decode
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[i] *= qk;
     // only the pages at the window start / sequence end hold invisible keys
+    // (their V rows are zeroed as operands too: the rows past the sequence end
+    // hold whatever the page held before, and 0 * NaN would be NaN)
+    uint32_t vmask_lo = ~0u, vmask_hi = ~0u;   // byte (e4m3) or half-word (bf16) masks
     if (page * kBlockSize < lo || page * kBlockSize + kBlockSize > L) {
+      uint32_t bits = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = page * kBlockSize + 4 * g + i;
-        s[i] = (key >= lo && key < L) ? s[i] : kNegInf;
+        const bool valid = key >= lo && key < L;
+        s[i] = valid ? s[i] : kNegInf;
+        bits |= valid ? 1u << i : 0u;
+      }
+      if constexpr (kFp8) {
+        vmask_lo = (bits & 1 ? 0xFFu : 0u) | (bits & 2 ? 0xFF00u : 0u) |
+                   (bits & 4 ? 0xFF0000u : 0u) | (bits & 8 ? 0xFF000000u : 0u);
+      } else {
+        vmask_lo = (bits & 1 ? 0xFFFFu : 0u) | (bits & 2 ? 0xFFFF0000u : 0u);
+        vmask_hi = (bits & 4 ? 0xFFFFu : 0u) | (bits & 8 ? 0xFFFF0000u : 0u);
       }
     }
     // ---- reference maximum -------------------------------------------------
@@ -372,8 +385,9 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFp8>())) void decode
           const int j = n >> 1;
           const i32x2 t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
               (lds_i32x2_ptr)(sv + (4 * g + (j & 3)) * RS + 16 * cb + 8 * (n & 1)));
-          const f16x2 v01 = e4m3x2_to_f16<false>((uint32_t)t[0]);
-          const f16x2 v23 = e4m3x2_to_f16<true>((uint32_t)t[0]);
+          const uint32_t codes = (uint32_t)t[0] & vmask_lo;
+          const f16x2 v01 = e4m3x2_to_f16<false>(codes);
+          const f16x2 v23 = e4m3x2_to_f16<true>(codes);
           const f16x4 vb = {v01[0], v01[1], v23[0], v23[1]};
           o[hh * BPS + cb] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vb, o[hh * BPS + cb], 0, 0, 0);
         }
@@ -395,8 +409,11 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFp8>())) void decode
           // lane j of the group addresses elements 16 cb + 4 (j & 3) .. +3 of
           // row 4g + (j >> 2); lane 4a + b receives element b of the pieces
           // of lanes a, a+4, a+8, a+12: column 16 cb + n of rows 4g .. 4g+3
-          const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          const s16x4 vr = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (lds_s16x4_ptr)(sv + (4 * g + (n >> 2)) * RS + 2 * (16 * cb + 4 * (n & 3))));
+          const i32x2 vw = __builtin_bit_cast(i32x2, vr);
+          const s16x4 vb = __builtin_bit_cast(
+              s16x4, i32x2{(int)((uint32_t)vw[0] & vmask_lo), (int)((uint32_t)vw[1] & vmask_hi)});
           f32x4 acc = o[hh * BPS + cb];
           acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vb, acc, 0, 0, 0);
           acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vb, acc, 0, 0, 0);

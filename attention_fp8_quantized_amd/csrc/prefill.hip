@@ -85,15 +85,22 @@ __device__ __forceinline__ float group4_sum(float v) {
   return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
+#ifndef FA8_PREFILL_ROW_SHIFT
+#define FA8_PREFILL_ROW_SHIFT 128   // extra LDS offset per 16 rows (bank spread of the V^T reads)
+#endif
+
 template <int D>
 __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(PrefillParams p) {
   constexpr int KQ = D / 32;               // 32-wide chunks of the head dim (bf16 MFMA K)
   constexpr int RS = D + 16;               // LDS row stride of the e4m3 K and V rows (bytes)
   constexpr int DB = D / 16;               // 16-wide output column blocks
-  __shared__ __attribute__((aligned(16))) uint8_t s_kv[2 * kTileN * RS];
+  // row r of a tile sits at r * RS + (r / 16) * FA8_PREFILL_ROW_SHIFT
+  constexpr int TB = kTileN * RS + (kTileN / 16) * FA8_PREFILL_ROW_SHIFT;   // bytes per K or V tile
+  auto row_at = [](int r) { return r * RS + (r >> 4) * FA8_PREFILL_ROW_SHIFT; };
+  __shared__ __attribute__((aligned(16))) uint8_t s_kv[2 * TB];
   __shared__ int s_bt[2][kTileN / kBlockSize];   // block ids of this tile and the next
   uint8_t* s_k = s_kv;
-  uint8_t* s_v = s_kv + kTileN * RS;
+  uint8_t* s_v = s_kv + TB;
 
   const int hq = blockIdx.y;
   const int b = blockIdx.z;
@@ -174,30 +181,46 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(PrefillParams p
     constexpr int CPH = kBlockSize * D / 16;          // chunks per page-half
     constexpr int CPT = 2 * PPT * CPH;                // chunks per tile
     static_assert(CPT % (64 * kWaves) == 0, "staging tiling");
-    constexpr int NCH = CPT / (64 * kWaves);          // chunks per thread
+    constexpr int NT = 64 * kWaves;
+    constexpr int NCH = CPT / NT;                     // chunks per thread
+    constexpr int HPI = NT / CPH;                     // page-halves per staging step
+    static_assert(NT % CPH == 0, "staging tiling");
     constexpr int BAT = NCH < 8 ? NCH : 8;            // chunks in flight per batch
+    // this thread's column chunk and row within every page-half it stages
+    const int my_ph = threadIdx.x / CPH;
+    const int within = threadIdx.x % CPH;
+    const uint8_t* src_base = p.cache + head_off + within * 16;
+    const int dst_off = (within / (D / 16)) * RS + (within % (D / 16)) * 16;
+    // only the last tile of a sequence can hold pages past its end, and rows
+    // past the end (zeroed here: they hold whatever the page held before,
+    // and 0 * NaN would be NaN in P.V)
+    const bool all_pages = (t + 1) * PPT <= n_pages;
+    const bool tail = (t + 1) * kTileN > L;
 #pragma unroll
     for (int k0 = 0; k0 < NCH; k0 += BAT) {
       uint4 val[BAT];
 #pragma unroll
       for (int k = 0; k < BAT; ++k) {
-        const int c = threadIdx.x + (k0 + k) * 64 * kWaves;
-        const int ph = c / CPH;                        // 0..PPT-1: K of page ph; PPT..: V
-        const int blk = s_bt[t & 1][ph % PPT];
-        val[k] = make_uint4(0, 0, 0, 0);
-        if (blk >= 0)
-          val[k] = *reinterpret_cast<const uint4*>(p.cache + (size_t)blk * blk_stride + head_off +
-                                                   (size_t)(ph / PPT) * kBlockSize * D +
-                                                   (c % CPH) * 16);
+        const int ph = (k0 + k) * HPI + my_ph;         // 0..PPT-1: K of page ph; PPT..: V
+        int blk = s_bt[t & 1][ph % PPT];
+        if constexpr (HPI == 1) blk = __builtin_amdgcn_readfirstlane(blk);
+        const uint8_t* src = src_base + (size_t)max(blk, 0) * blk_stride +
+                             (ph / PPT) * kBlockSize * D;
+        if (all_pages) {
+          val[k] = *reinterpret_cast<const uint4*>(src);
+        } else {
+          val[k] = make_uint4(0, 0, 0, 0);
+          if (blk >= 0) val[k] = *reinterpret_cast<const uint4*>(src);
+        }
       }
 #pragma unroll
       for (int k = 0; k < BAT; ++k) {
-        const int c = threadIdx.x + (k0 + k) * 64 * kWaves;
-        const int ph = c / CPH;
-        const int within = c % CPH;
-        const int row = (ph % PPT) * kBlockSize + within / (D / 16);
-        *reinterpret_cast<uint4*>((ph / PPT ? s_v : s_k) + row * RS + (within % (D / 16)) * 16) =
-            val[k];
+        const int ph = (k0 + k) * HPI + my_ph;
+        const int pg = ph % PPT;
+        if (tail && t * kTileN + pg * kBlockSize + within / (D / 16) >= L) val[k] = make_uint4(0, 0, 0, 0);
+        // row pg*16 + r sits at (pg*16 + r) * RS + pg * FA8_PREFILL_ROW_SHIFT
+        *reinterpret_cast<uint4*>((ph / PPT ? s_v : s_k) + pg * (kBlockSize * RS + FA8_PREFILL_ROW_SHIFT) +
+                                  dst_off) = val[k];
       }
     }
     // the next tile's block ids, requested now and stored after this tile's
@@ -214,20 +237,29 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(PrefillParams p
     // to bf16 (exact)
     f32x4 s[8];
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mb = 0; mb < 8; ++mb) s[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // key blocks are independent accumulation chains: interleave them in
+    // groups of QKI
+#ifndef FA8_PREFILL_QK_CHAINS
+#define FA8_PREFILL_QK_CHAINS 2
+#endif
+    constexpr int QKI = FA8_PREFILL_QK_CHAINS;
+#pragma unroll
+    for (int mb0 = 0; mb0 < 8; mb0 += QKI) {
 #pragma unroll
       for (int kq = 0; kq < KQ; ++kq) {
-        const uint2 a = *reinterpret_cast<const uint2*>(s_k + (16 * mb + n) * RS + kq * 32 + g * 8);
-        const bf16x2 a0 = e4m3x2_to_bf16<false>(a.x), a1 = e4m3x2_to_bf16<true>(a.x);
-        const bf16x2 a2 = e4m3x2_to_bf16<false>(a.y), a3 = e4m3x2_to_bf16<true>(a.y);
-        const bf16x8 av = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[kq], acc, 0, 0, 0);
+#pragma unroll
+        for (int mb = mb0; mb < mb0 + QKI; ++mb) {
+          const uint2 a = *reinterpret_cast<const uint2*>(s_k + row_at(16 * mb + n) + kq * 32 + g * 8);
+          const bf16x2 a0 = e4m3x2_to_bf16<false>(a.x), a1 = e4m3x2_to_bf16<true>(a.x);
+          const bf16x2 a2 = e4m3x2_to_bf16<false>(a.y), a3 = e4m3x2_to_bf16<true>(a.y);
+          const bf16x8 av = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+          s[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[kq], s[mb], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // bounds the operand reads in flight
       }
-      s[mb] = acc;
     }
 
-    // ---- scale, mask, tile maximum ------------------------------------------
     // tiles wholly visible to every row of the block skip the mask
     const int k_first = t * kTileN, k_last = k_first + kTileN - 1;
     const bool full = k_last <= P0 + q0 && q0 + kBlockM <= T &&
@@ -283,28 +315,48 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(PrefillParams p
     for (int i = 0; i < 4; ++i) alpha_o[i] = __shfl(alpha, 4 * g + i);
 
     // ---- P~ . V~ per 16-column block -------------------------------------------
+    // row j = n/2 of read r is key kappa(g, 8r + j); lanes 2j, 2j+1 give the
+    // two 8-byte halves of the block's 16 columns
+    const int j = n >> 1;
+    const uint8_t* vrow[4];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int r = 0; r < 4; ++r)
+      vrow[r] = s_v + row_at(32 * r + 16 * (j >> 2) + 4 * g + (j & 3)) + (n & 1) * 8;
+    auto load_vb = [&](int db) {
       i32x8 vb;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        // row j = n/2 of read r is key kappa(g, 8r + j); lanes 2j, 2j+1 give
-        // the two 8-byte halves of the block's 16 columns
-        const int j = n >> 1;
-        const int key = 32 * r + 16 * (j >> 2) + 4 * g + (j & 3);
-        const i32x2 v2 = lds_read_tr8(s_v + key * RS + 16 * db + (n & 1) * 8);
+        const i32x2 v2 = lds_read_tr8(vrow[r] + 16 * db);
         vb[2 * r] = v2[0];
         vb[2 * r + 1] = v2[1];
       }
-      if (p.accum_mode == 1) {
+      return vb;
+    };
+    // software pipeline: the next block's V^T reads are in flight while this
+    // block's product runs.  The accumulation mode is tested once per tile.
+    if (p.accum_mode == 1) {
+      i32x8 vb_next = load_vb(0);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const i32x8 vb = vb_next;
+        if (db + 1 < DB) vb_next = load_vb(db + 1);
+        // level 1: this tile's P.V into a zeroed accumulator; level 2: fp32 flush
         const f32x4 acc = mfma_fp8(pa, vb, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[db][i] = alpha_o[i] * o[db][i] + acc[i];
-      } else {
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      i32x8 vb_next = load_vb(0);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const i32x8 vb = vb_next;
+        if (db + 1 < DB) vb_next = load_vb(db + 1);
         f32x4 c;
 #pragma unroll
         for (int i = 0; i < 4; ++i) c[i] = alpha_o[i] * o[db][i];
         o[db] = mfma_fp8(pa, vb, c);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (threadIdx.x < PPT && t < t_hi) s_bt[(t + 1) & 1][threadIdx.x] = next_blk;
@@ -325,13 +377,18 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(PrefillParams p
   }
 }
 
+template <int D>
+static void launch_prefill_d(const PrefillParams& p, dim3 grid, dim3 block, hipStream_t stream) {
+  hipLaunchKernelGGL(prefill_kernel<D>, grid, block, 0, stream, p);
+}
+
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   dim3 grid((p.max_q_len + kBlockM - 1) / kBlockM, p.num_q_heads, p.batch);
   dim3 block(64 * kWaves);
   switch (p.head_dim) {
-    case 64: hipLaunchKernelGGL(prefill_kernel<64>, grid, block, 0, stream, p); break;
-    case 128: hipLaunchKernelGGL(prefill_kernel<128>, grid, block, 0, stream, p); break;
-    case 256: hipLaunchKernelGGL(prefill_kernel<256>, grid, block, 0, stream, p); break;
+    case 64: launch_prefill_d<64>(p, grid, block, stream); break;
+    case 128: launch_prefill_d<128>(p, grid, block, stream); break;
+    case 256: launch_prefill_d<256>(p, grid, block, stream); break;
     default: return hipErrorNotSupported;
   }
   return hipGetLastError();

@@ -62,7 +62,7 @@ class DecodeCase:
 
     def __init__(self, B, Hq, Hkv, D, lens, cache_dtype="e4m3", seed=0,
                  outliers=False, scales="absmax", window=0, oracle_heads=None,
-                 q_zero=False):
+                 q_zero=False, fill=0):
         import torch
         import attention_fp8_quantized_amd as fa
         self.B, self.Hq, self.Hkv, self.D = B, Hq, Hkv, D
@@ -93,8 +93,10 @@ class DecodeCase:
                                    else W.normal(W.rng(seed, 0, W.Q), (B, Hq, D)))
         self.k, self.v = k, v
         # GPU side
+        # cache bytes before the writes: rows past each sequence end keep
+        # them (0xFF is a NaN code in e4m3 and a NaN half-word in bf16)
         self.cache = fa.new_cache(max(self.nblocks, 1), Hkv, D, cache_dtype)
-        self.cache.view(torch.uint8).fill_(0)
+        self.cache.view(torch.uint8).fill_(fill)
         if N:
             fa.cache_write(dev(k), dev(v), dev(self.slots), dev(self.ks), dev(self.vs),
                            self.cache)
@@ -148,7 +150,7 @@ class PrefillCase:
     lens[b] whose last qlens[b] tokens are the queries (packed by cu)."""
 
     def __init__(self, qlens, lens, Hq, Hkv, D, seed=0, window=0, q_zero=False,
-                 q_scale="absmax"):
+                 q_scale="absmax", fill=0):
         import torch
         import attention_fp8_quantized_amd as fa
         self.qlens = np.asarray(qlens, dtype=np.int32)
@@ -177,7 +179,7 @@ class PrefillCase:
             self.qs = np.array([q_scale], np.float32)
         self.k, self.v = k, v
         self.cache = fa.new_cache(self.nblocks, Hkv, D, "e4m3")
-        self.cache.view(torch.uint8).fill_(0)
+        self.cache.view(torch.uint8).fill_(fill)
         fa.cache_write(dev(k), dev(v), dev(self.slots), dev(self.ks), dev(self.vs), self.cache)
         self.q_dev = qb.cuda()
         self.dev = {n: dev(a) for n, a in dict(cu=self.cu, bt=self.bt, lens=self.lens,

@@ -78,6 +78,17 @@ def test_split_count_invariance(cd):
         assert rl < tol, (s, rl)
 
 
+@pytest.mark.parametrize("cd", ["e4m3", "bf16"])
+@pytest.mark.parametrize("window", [0, 100])
+def test_stale_nan_rows_past_sequence_end(cd, window):
+    # pages are pre-filled with NaN codes; the rows past each sequence end
+    # (and before the window start) keep them and must not reach the output
+    lens = [1000, 37, 5, 129]
+    c = DecodeCase(len(lens), 16, 2, 128, lens, cd, seed=33, window=window, fill=0xFF)
+    got = _check(c, f"stale NaN rows {cd} window={window}")
+    assert np.all(np.isfinite(got))
+
+
 def test_page_permutation_invariance():
     import torch
     c = DecodeCase(1, 32, 8, 128, [4000], "e4m3", seed=31)

@@ -43,6 +43,17 @@ def test_chunked_ragged_batch_gqa(window):
     assert_gate(c.run_gpu(), ref, f"ragged batch window={window}", slack=slack)
 
 
+def test_stale_nan_rows_past_sequence_end():
+    # pages are pre-filled with NaN codes; the rows past each sequence end
+    # keep them and must not reach the output
+    c = PrefillCase([130, 75], [130, 333], 4, 2, 128, seed=8, fill=0xFF)
+    log("prefill stale NaN rows")
+    got = c.run_gpu()
+    assert np.all(np.isfinite(got))
+    ref, slack = c.oracle()
+    assert_gate(got, ref, "stale NaN rows", slack=slack)
+
+
 def test_uniform_scores_mean_of_visible_v():
     from oracle import e4m3
     c = PrefillCase([70], [150], 2, 1, 64, seed=9, q_zero=True, q_scale=1.0)
