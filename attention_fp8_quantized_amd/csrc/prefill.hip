@@ -39,6 +39,8 @@
 //     instead lets the MFMA accumulate into alpha*O.
 // Epilogue: out = O * v_scale / l.
 
+#include <type_traits>
+
 #include "fa8_device.hpp"
 #include "fa8_internal.hpp"
 
@@ -46,7 +48,7 @@ namespace fa8 {
 
 constexpr int kTileN = 128;      // keys per KV tile
 constexpr int kWaveRows = 16;    // query rows per wave
-constexpr int kWaves = 4;        // waves per workgroup
+constexpr int kWaves = 8;        // waves per workgroup
 constexpr int kBlockM = kWaveRows * kWaves;
 constexpr float kNegInfP = -__builtin_huge_valf();
 
@@ -85,22 +87,33 @@ __device__ __forceinline__ float group4_sum(float v) {
   return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
-#ifndef FA8_PREFILL_ROW_SHIFT
-#define FA8_PREFILL_ROW_SHIFT 128   // extra LDS offset per 16 rows (bank spread of the V^T reads)
-#endif
+// LDS layout of a staged tile: rows of D bytes, no padding; the 16-byte
+// chunk c of row r sits at chunk position c ^ sw(r).  sw spreads the rows an
+// operand read touches over the 64 banks: the K operand reads 16 consecutive
+// rows, the transposed V reads rows 4g..4g+3 and 16+4g..16+4g+3.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  constexpr int CPR = D / 16;              // chunks per row
+  constexpr int RPB = 256 / D;             // rows per 256-byte bank period
+  return ((r / RPB) % CPR) ^ (((r >> 4) & 1) * (CPR / 2));
+}
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 template <int D>
-__global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
   constexpr int KQ = D / 32;               // 32-wide chunks of the head dim (bf16 MFMA K)
-  constexpr int RS = D + 16;               // LDS row stride of the e4m3 K and V rows (bytes)
   constexpr int DB = D / 16;               // 16-wide output column blocks
-  // row r of a tile sits at r * RS + (r / 16) * FA8_PREFILL_ROW_SHIFT
-  constexpr int TB = kTileN * RS + (kTileN / 16) * FA8_PREFILL_ROW_SHIFT;   // bytes per K or V tile
-  auto row_at = [](int r) { return r * RS + (r >> 4) * FA8_PREFILL_ROW_SHIFT; };
-  __shared__ __attribute__((aligned(16))) uint8_t s_kv[2 * TB];
-  __shared__ int s_bt[2][kTileN / kBlockSize];   // block ids of this tile and the next
-  uint8_t* s_k = s_kv;
-  uint8_t* s_v = s_kv + TB;
+  constexpr int TILE = kTileN * D;         // bytes of one staged K (or V) tile
+  constexpr int PPT = kTileN / kBlockSize; // pages per tile
+  constexpr int RPI = 1024 / D;            // rows per wave-wide 16-byte-per-lane copy
+  constexpr int NCOPY = 2 * TILE / 1024 / kWaves;   // copies per wave per tile
+  static_assert(NCOPY >= 1 && kBlockSize % RPI == 0, "staging tiling");
+  // two tile buffers (K then V), filled by direct global->LDS copies while
+  // the other one is being computed on
+  __shared__ __attribute__((aligned(16))) uint8_t s_buf0[2 * TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t s_buf1[2 * TILE];
+  __shared__ int s_bt[4][PPT];             // block ids of tiles t .. t+3 (ring)
 
   const int hq = blockIdx.y;
   const int b = blockIdx.z;
@@ -115,7 +128,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(PrefillParams p
   const int L = p.seq_lens[b];
   const int P0 = L - T;                    // position of the chunk's first query
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;                 // lane group (k-slot group of the MFMA)
   const int n = lane & 15;                 // query (S^T, P) or column (V, O) of the lane
   const int row = q0 + wave * kWaveRows + n;   // this lane's query row (S^T layout)
@@ -143,6 +156,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(PrefillParams p
       qb[kq][2 * h2] = d2[0];
       qb[kq][2 * h2 + 1] = d2[1];
     }
+    __builtin_amdgcn_sched_barrier(0);   // one chunk at a time (register pressure)
   }
   // log2-domain score multiplier
   const float qk = qsc * p.k_scale[h] * p.sm_scale * kLog2e;
@@ -165,99 +179,96 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(PrefillParams p
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // block ids of the first tile (pages past the sequence end: -1)
-  constexpr int PPT = kTileN / kBlockSize;          // pages per tile
-  if (threadIdx.x < PPT) {
-    const int page = t_lo * PPT + threadIdx.x;
-    s_bt[t_lo & 1][threadIdx.x] = page < n_pages ? bt[page] : -1;
-  }
-  for (int t = t_lo; t <= t_hi; ++t) {
-    // ---- stage the tile's K and V rows (e4m3) in LDS ----------------------------
-    // chunk c of the tile: page-half c / (16*D/16) (K pages, then V pages),
-    // 16 bytes each; consecutive threads take consecutive chunks of a
-    // page-half, so every load instruction reads whole rows.  Zeros past the
-    // end of the sequence.
-    __syncthreads();
-    constexpr int CPH = kBlockSize * D / 16;          // chunks per page-half
-    constexpr int CPT = 2 * PPT * CPH;                // chunks per tile
-    static_assert(CPT % (64 * kWaves) == 0, "staging tiling");
-    constexpr int NT = 64 * kWaves;
-    constexpr int NCH = CPT / NT;                     // chunks per thread
-    constexpr int HPI = NT / CPH;                     // page-halves per staging step
-    static_assert(NT % CPH == 0, "staging tiling");
-    constexpr int BAT = NCH < 8 ? NCH : 8;            // chunks in flight per batch
-    // this thread's column chunk and row within every page-half it stages
-    const int my_ph = threadIdx.x / CPH;
-    const int within = threadIdx.x % CPH;
-    const uint8_t* src_base = p.cache + head_off + within * 16;
-    const int dst_off = (within / (D / 16)) * RS + (within % (D / 16)) * 16;
-    // only the last tile of a sequence can hold pages past its end, and rows
-    // past the end (zeroed here: they hold whatever the page held before,
-    // and 0 * NaN would be NaN in P.V)
-    const bool all_pages = (t + 1) * PPT <= n_pages;
-    const bool tail = (t + 1) * kTileN > L;
+  // block id of page `page` of the sequence (pages past the end: page 0's;
+  // their V rows are zeroed after the copy)
+  auto page_blk = [&](int page) { return bt[page < n_pages ? page : 0]; };
+  // Copy u of this wave (0..NCOPY-1) fills rows row0 .. row0+RPI-1 of the K
+  // (first TILE bytes) or V tile, one 16-byte chunk per lane.  With 8 waves
+  // the row of a lane within its page, and so its swizzle, is the same for
+  // every copy: the per-lane source offset is computed once, and each copy
+  // adds the (uniform) page address.
+  static_assert(kWaves == 8, "copy mapping");
+  const int my_r = (wave * RPI) % kBlockSize + lane / (D / 16);   // row within the page
+  const int my_r16 = (wave * RPI / kBlockSize) & 1;                // bit 4 of the tile row
+  const int lane_off = my_r * D + ((lane % (D / 16)) ^ swz<D>(my_r + 16 * my_r16)) * 16;
+  auto stage = [&](uint8_t* buf, int slot) {
+    // opaque per call, so that the compiler keeps one 32-bit lane offset and
+    // uniform page addresses instead of hoisting a 64-bit address per copy
+    int voff = lane_off;
+    asm volatile("" : "+v"(voff));
 #pragma unroll
-    for (int k0 = 0; k0 < NCH; k0 += BAT) {
-      uint4 val[BAT];
-#pragma unroll
-      for (int k = 0; k < BAT; ++k) {
-        const int ph = (k0 + k) * HPI + my_ph;         // 0..PPT-1: K of page ph; PPT..: V
-        int blk = s_bt[t & 1][ph % PPT];
-        if constexpr (HPI == 1) blk = __builtin_amdgcn_readfirstlane(blk);
-        const uint8_t* src = src_base + (size_t)max(blk, 0) * blk_stride +
-                             (ph / PPT) * kBlockSize * D;
-        if (all_pages) {
-          val[k] = *reinterpret_cast<const uint4*>(src);
-        } else {
-          val[k] = make_uint4(0, 0, 0, 0);
-          if (blk >= 0) val[k] = *reinterpret_cast<const uint4*>(src);
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < BAT; ++k) {
-        const int ph = (k0 + k) * HPI + my_ph;
-        const int pg = ph % PPT;
-        if (tail && t * kTileN + pg * kBlockSize + within / (D / 16) >= L) val[k] = make_uint4(0, 0, 0, 0);
-        // row pg*16 + r sits at (pg*16 + r) * RS + pg * FA8_PREFILL_ROW_SHIFT
-        *reinterpret_cast<uint4*>((ph / PPT ? s_v : s_k) + pg * (kBlockSize * RS + FA8_PREFILL_ROW_SHIFT) +
-                                  dst_off) = val[k];
-      }
+    for (int u = 0; u < NCOPY; ++u) {
+      const int idx = u * kWaves + wave;                 // 0 .. 2*TILE/1024-1
+      const int kv = idx / (TILE / 1024);
+      const int row0 = (idx % (TILE / 1024)) * RPI;      // first row (within the tile)
+      const int blk = __builtin_amdgcn_readfirstlane(s_bt[slot][row0 / kBlockSize]);
+      const uint8_t* page = p.cache + (size_t)blk * blk_stride + head_off +
+                            (size_t)kv * kBlockSize * D;
+      __builtin_amdgcn_global_load_lds(page + voff, (lds_void_ptr)(buf + kv * TILE + row0 * D), 16,
+                                       0, 0);
     }
-    // the next tile's block ids, requested now and stored after this tile's
-    // compute (its slot is not read during this tile)
-    int next_blk = -1;
-    if (threadIdx.x < PPT && t < t_hi) {
-      const int page = (t + 1) * PPT + threadIdx.x;
-      next_blk = page < n_pages ? bt[page] : -1;
-    }
-    __syncthreads();
+  };
 
+  // block ids of the first two tiles
+  if (threadIdx.x < 2 * PPT) {
+    const int t = t_lo + threadIdx.x / PPT;
+    s_bt[t & 3][threadIdx.x % PPT] = page_blk(t * PPT + threadIdx.x % PPT);
+  }
+  __syncthreads();
+  stage(s_buf0, t_lo & 3);
+
+  // One tile.  kOdd selects the buffer roles at compile time (the tile loop is
+  // unrolled by two), so the compiler sees that the copies in flight target
+  // the other buffer than the one being read.
+  auto tile_step = [&](auto odd_tag, int t) {
+    constexpr bool kOdd = decltype(odd_tag)::value;
+    uint8_t* cur = kOdd ? s_buf1 : s_buf0;
+    uint8_t* nxt = kOdd ? s_buf0 : s_buf1;
+    const uint8_t* s_k = cur;
+    const uint8_t* s_v = cur + TILE;
+    // block ids of tile t+2 (every thread loads one, so that the number of
+    // copies in flight is the same in every lane)
+    const int nb_page = (t + 2) * PPT + (threadIdx.x % PPT);
+    const int next_blk = page_blk(nb_page);
+    // the next tile's copies (after the last tile: a tile past the end, all
+    // zero rows, never read), then wait for this tile's copies: everything
+    // but the id load and the NCOPY copies just issued
+    stage(nxt, (t + 1) & 3);
+    __builtin_amdgcn_s_waitcnt(0x3F70 | (NCOPY + 1));
+    // rows past the sequence end (the tail tile only): every lane overwrites
+    // the V chunks it copied with zeros before the barrier publishes them
+    if ((t + 1) * kTileN > L) {
+      const int rows_left = L - t * kTileN;
+#pragma unroll
+      for (int u = 0; u < NCOPY; ++u) {
+        const int idx = u * kWaves + wave;
+        const int row0 = (idx % (TILE / 1024)) * RPI;
+        if (idx / (TILE / 1024) == 1 && row0 + lane / (D / 16) >= rows_left)
+          *reinterpret_cast<uint4*>(cur + TILE + row0 * D + lane * 16) = make_uint4(0, 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
     // ---- S^T = K . Q^T : 8 blocks of 16 keys -----------------------------------
-    // the A operand: 8 K codes of key 16 mb + n, columns 32 kq + 8 g, widened
-    // to bf16 (exact)
+    // the A operand: 8 K codes of key 16 mb + n, columns 32 kq + 8 g,
+    // widened to bf16 (exact)
     f32x4 s[8];
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) s[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // key blocks are independent accumulation chains: interleave them in
-    // groups of QKI
-#ifndef FA8_PREFILL_QK_CHAINS
-#define FA8_PREFILL_QK_CHAINS 2
-#endif
-    constexpr int QKI = FA8_PREFILL_QK_CHAINS;
 #pragma unroll
-    for (int mb0 = 0; mb0 < 8; mb0 += QKI) {
+    for (int mb = 0; mb < 8; ++mb) {
+      const int kr = 16 * mb + n;
+      const uint8_t* krow = s_k + kr * D + 8 * (g & 1);
+      const int ksw = swz<D>(kr);
 #pragma unroll
       for (int kq = 0; kq < KQ; ++kq) {
-#pragma unroll
-        for (int mb = mb0; mb < mb0 + QKI; ++mb) {
-          const uint2 a = *reinterpret_cast<const uint2*>(s_k + row_at(16 * mb + n) + kq * 32 + g * 8);
-          const bf16x2 a0 = e4m3x2_to_bf16<false>(a.x), a1 = e4m3x2_to_bf16<true>(a.x);
-          const bf16x2 a2 = e4m3x2_to_bf16<false>(a.y), a3 = e4m3x2_to_bf16<true>(a.y);
-          const bf16x8 av = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-          s[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[kq], s[mb], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);   // bounds the operand reads in flight
+        const uint2 a = *reinterpret_cast<const uint2*>(krow + (((2 * kq + (g >> 1)) ^ ksw) * 16));
+        const bf16x2 a0 = e4m3x2_to_bf16<false>(a.x), a1 = e4m3x2_to_bf16<true>(a.x);
+        const bf16x2 a2 = e4m3x2_to_bf16<false>(a.y), a3 = e4m3x2_to_bf16<true>(a.y);
+        const bf16x8 av = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+        s[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[kq], s[mb], 0, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     // tiles wholly visible to every row of the block skip the mask
@@ -314,19 +325,24 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(PrefillParams p
 #pragma unroll
     for (int i = 0; i < 4; ++i) alpha_o[i] = __shfl(alpha, 4 * g + i);
 
+    __builtin_amdgcn_sched_barrier(0);
     // ---- P~ . V~ per 16-column block -------------------------------------------
     // row j = n/2 of read r is key kappa(g, 8r + j); lanes 2j, 2j+1 give the
     // two 8-byte halves of the block's 16 columns
     const int j = n >> 1;
     const uint8_t* vrow[4];
+    int vsw[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      vrow[r] = s_v + row_at(32 * r + 16 * (j >> 2) + 4 * g + (j & 3)) + (n & 1) * 8;
+    for (int r = 0; r < 4; ++r) {
+      const int kr = 32 * r + 16 * (j >> 2) + 4 * g + (j & 3);
+      vrow[r] = s_v + kr * D + (n & 1) * 8;
+      vsw[r] = swz<D>(kr);
+    }
     auto load_vb = [&](int db) {
       i32x8 vb;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const i32x2 v2 = lds_read_tr8(vrow[r] + 16 * db);
+        const i32x2 v2 = lds_read_tr8(vrow[r] + ((db ^ vsw[r]) * 16));
         vb[2 * r] = v2[0];
         vb[2 * r + 1] = v2[1];
       }
@@ -359,7 +375,15 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(PrefillParams p
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (threadIdx.x < PPT && t < t_hi) s_bt[(t + 1) & 1][threadIdx.x] = next_blk;
+    if (threadIdx.x < PPT) s_bt[(t + 2) & 3][threadIdx.x] = next_blk;
+    // every wave is done with this buffer (the next copies into it start
+    // after this barrier) and the block ids are visible
+    __syncthreads();
+  };
+
+  for (int t = t_lo; t <= t_hi; t += 2) {
+    tile_step(std::false_type{}, t);
+    if (t + 1 <= t_hi) tile_step(std::true_type{}, t + 1);
   }
 
   // ---- epilogue: out = O * v_scale / l ---------------------------------------
