@@ -227,12 +227,11 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast(bf16x8, w); }
 
-// Waves per SIMD the register budget is sized for (without spills): four
-// (two 8-wave workgroups per CU) where a page fits, fewer for the larger
-// pages of the bf16 cache and of head_dim 256.
+// Waves per SIMD the register budget is sized for, without spills: four at
+// head_dim 64, three at 128, two at 256.
 template <int D, bool kFp8>
 constexpr int decode_min_waves() {
-  return D == 256 ? 2 : (kFp8 || D == 64) ? 4 : 3;
+  return D == 64 ? 4 : D == 128 ? 3 : 2;
 }
 
 template <int D, int G, bool kFp8, int NW, int PD>

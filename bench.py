@@ -484,6 +484,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also launch the plain copy kernel (for counter calibration)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the head_dim-256 leg (prefill + 128k decode); prints its JSON")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
@@ -494,6 +496,9 @@ def main():
     import attention_fp8_quantized_amd as fa
     fa.load()
     torch.cuda.init()
+    if args.prefill_only:
+        print(json.dumps({"hd256": measure_hd256(fa, torch)}), flush=True)
+        return
 
     B, Hq, Hkv, D, ctx, layers = 1, 32, 8, 128, args.ctx, args.layers
     log(f"filling {layers} FP8 layers x {ctx} tokens")
