@@ -17,7 +17,8 @@ import os
 __all__ = [
     "FA8_F32", "FA8_BF16", "FA8_E4M3", "BLOCK_SIZE", "Fa8Error", "library_path",
     "load", "cache_write", "decode_num_splits", "decode_workspace_bytes",
-    "decode_attention", "prefill_kv_tile", "prefill_attention", "new_cache",
+    "decode_attention", "decode_attention_append", "prefill_kv_tile", "prefill_attention",
+    "new_cache",
     "new_decode_workspace",
 ]
 
@@ -48,6 +49,9 @@ _SIGNATURES = {
     "fa8_decode_attention": (_I32, [_VP, _I32, _I32, _VP, _I32, _I64, _I32, _I32, _VP,
                                     _I32, _VP, _I32, _VP, _VP, _F32, _I32, _I32, _VP,
                                     _VP, _SZ, _VP]),
+    "fa8_decode_attention_append": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _VP, _I32, _I64,
+                                            _I32, _I32, _VP, _I32, _VP, _I32, _VP, _VP, _F32,
+                                            _I32, _I32, _VP, _VP, _SZ, _VP]),
     "fa8_prefill_kv_tile": (_I32, [_I32]),
     "fa8_prefill_attention": (_I32, [_VP, _VP, _I32, _I32, _I32, _VP, _I64, _I32, _I32,
                                      _VP, _I32, _VP, _VP, _VP, _VP, _F32, _I32, _I32,
@@ -177,14 +181,8 @@ def new_decode_workspace(nbytes, device="cuda"):
     return torch.zeros(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
 
-def decode_attention(q, cache, block_table, seq_lens, k_scale, v_scale, sm_scale,
-                     max_seq_len, window=0, num_splits=0, out=None, workspace=None):
-    """One decode step. q bf16 [B][H_q][D] -> out fp32 [B][H_q][D].
-
-    ``max_seq_len`` is a host-side upper bound of ``seq_lens`` (sizes the
-    grid).  ``workspace`` (uint8 device tensor from ``new_decode_workspace``)
-    is allocated here when not given; pass one to keep the call
-    allocation-free."""
+def _decode_args(q, cache, block_table, seq_lens, k_scale, v_scale, max_seq_len, window,
+                 num_splits, out, workspace):
     torch = _torch()
     _require(cache, "cache", ndim=5)
     dev = cache.device
@@ -201,7 +199,6 @@ def decode_attention(q, cache, block_table, seq_lens, k_scale, v_scale, sm_scale
     if cdt == FA8_E4M3:
         _require(k_scale, "k_scale", dtype=torch.float32, device=dev, ndim=1)
         _require(v_scale, "v_scale", dtype=torch.float32, device=dev, ndim=1)
-    lib = load()
     splits = num_splits or decode_num_splits(B, hkv, int(max_seq_len), int(window))
     need = decode_workspace_bytes(B, hq, d, splits)
     if workspace is None:
@@ -212,13 +209,55 @@ def decode_attention(q, cache, block_table, seq_lens, k_scale, v_scale, sm_scale
         out = torch.empty((B, hq, d), dtype=torch.float32, device=dev)
     else:
         _require(out, "out", dtype=torch.float32, device=dev, ndim=3)
+    head = (_ptr(q),)
+    tail = (B, hq, _ptr(cache), cdt, nb, hkv, d, _ptr(block_table), block_table.shape[1],
+            _ptr(seq_lens), int(max_seq_len),
+            _ptr(k_scale) if cdt == FA8_E4M3 else None,
+            _ptr(v_scale) if cdt == FA8_E4M3 else None)
+    return head, tail, splits, out, workspace
+
+
+def decode_attention(q, cache, block_table, seq_lens, k_scale, v_scale, sm_scale,
+                     max_seq_len, window=0, num_splits=0, out=None, workspace=None):
+    """One decode step. q bf16 [B][H_q][D] -> out fp32 [B][H_q][D].
+
+    ``max_seq_len`` is a host-side upper bound of ``seq_lens`` (sizes the
+    grid).  ``workspace`` (uint8 device tensor from ``new_decode_workspace``)
+    is allocated here when not given; pass one to keep the call
+    allocation-free."""
+    lib = load()
+    head, tail, splits, out, workspace = _decode_args(
+        q, cache, block_table, seq_lens, k_scale, v_scale, max_seq_len, window, num_splits,
+        out, workspace)
     _check(lib.fa8_decode_attention(
-        _ptr(q), B, hq, _ptr(cache), cdt, nb, hkv, d, _ptr(block_table),
-        block_table.shape[1], _ptr(seq_lens), int(max_seq_len),
-        _ptr(k_scale) if cdt == FA8_E4M3 else None,
-        _ptr(v_scale) if cdt == FA8_E4M3 else None,
-        float(sm_scale), int(window), int(splits), _ptr(out), _ptr(workspace),
+        *head, *tail, float(sm_scale), int(window), int(splits), _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(cache)))
+    return out
+
+
+def decode_attention_append(q, k_new, v_new, cache, block_table, seq_lens, k_scale, v_scale,
+                            sm_scale, max_seq_len, window=0, num_splits=0, out=None,
+                            workspace=None):
+    """Fused decode step: writes k_new / v_new ([B][H_kv][D], fp32 or bf16)
+    as token seq_lens[b]-1 of each sequence (the bytes cache_write would
+    store) and attends over the context including it."""
+    torch = _torch()
+    lib = load()
+    head, tail, splits, out, workspace = _decode_args(
+        q, cache, block_table, seq_lens, k_scale, v_scale, max_seq_len, window, num_splits,
+        out, workspace)
+    B, hkv, d = q.shape[0], cache.shape[1], cache.shape[4]
+    if k_new.dtype not in (torch.float32, torch.bfloat16) or v_new.dtype != k_new.dtype:
+        raise ValueError("k_new / v_new must both be float32 or both bfloat16")
+    for t, name in ((k_new, "k_new"), (v_new, "v_new")):
+        _require(t, name, device=cache.device, ndim=3)
+        if tuple(t.shape) != (B, hkv, d):
+            raise ValueError(f"{name} must be [batch, num_kv_heads, head_dim]")
+    in_dtype = FA8_BF16 if k_new.dtype == torch.bfloat16 else FA8_F32
+    _check(lib.fa8_decode_attention_append(
+        head[0], _ptr(k_new), _ptr(v_new), in_dtype, *tail, float(sm_scale), int(window),
+        int(splits), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(cache)))
     return out
 
 

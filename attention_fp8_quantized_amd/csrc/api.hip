@@ -131,14 +131,15 @@ size_t fa8_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t he
   return fa8::decode_workspace_bytes(batch, num_q_heads, head_dim, num_splits);
 }
 
-fa8_status fa8_decode_attention(const void* q, int32_t batch, int32_t num_q_heads,
-                                const void* cache, int32_t cache_dtype, int64_t num_blocks,
-                                int32_t num_kv_heads, int32_t head_dim,
-                                const int32_t* block_table, int32_t max_blocks_per_seq,
-                                const int32_t* seq_lens, int32_t max_seq_len,
-                                const float* k_scale, const float* v_scale, float sm_scale,
-                                int32_t window, int32_t num_splits, float* out,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+static fa8_status decode_impl(const void* q, int32_t batch, int32_t num_q_heads,
+                              const void* cache, int32_t cache_dtype, int64_t num_blocks,
+                              int32_t num_kv_heads, int32_t head_dim,
+                              const int32_t* block_table, int32_t max_blocks_per_seq,
+                              const int32_t* seq_lens, int32_t max_seq_len,
+                              const float* k_scale, const float* v_scale, float sm_scale,
+                              int32_t window, int32_t num_splits, float* out,
+                              void* workspace, size_t workspace_bytes, void* stream,
+                              const void* k_new, const void* v_new, int32_t new_dtype) {
   if (batch < 0) return fail(FA8_EINVAL, "decode: batch < 0");
   if (num_q_heads <= 0 || num_kv_heads <= 0)
     return fail(FA8_EINVAL, "decode: head counts must be > 0");
@@ -197,10 +198,47 @@ fa8_status fa8_decode_attention(const void* q, int32_t batch, int32_t num_q_head
   p.window = window > 0 ? window : 0;
   p.fp8 = cache_dtype == FA8_E4M3 ? 1 : 0;
   p.sm_scale = sm_scale;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.new_bf16 = new_dtype == FA8_BF16 ? 1 : 0;
   const hipError_t e =
       fa8::launch_decode(p, cache_dtype == FA8_E4M3, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
+}
+
+fa8_status fa8_decode_attention(const void* q, int32_t batch, int32_t num_q_heads,
+                                const void* cache, int32_t cache_dtype, int64_t num_blocks,
+                                int32_t num_kv_heads, int32_t head_dim,
+                                const int32_t* block_table, int32_t max_blocks_per_seq,
+                                const int32_t* seq_lens, int32_t max_seq_len,
+                                const float* k_scale, const float* v_scale, float sm_scale,
+                                int32_t window, int32_t num_splits, float* out,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(q, batch, num_q_heads, cache, cache_dtype, num_blocks, num_kv_heads,
+                     head_dim, block_table, max_blocks_per_seq, seq_lens, max_seq_len, k_scale,
+                     v_scale, sm_scale, window, num_splits, out, workspace, workspace_bytes,
+                     stream, nullptr, nullptr, FA8_F32);
+}
+
+fa8_status fa8_decode_attention_append(const void* q, const void* k_new, const void* v_new,
+                                       int32_t in_dtype, int32_t batch, int32_t num_q_heads,
+                                       void* cache, int32_t cache_dtype, int64_t num_blocks,
+                                       int32_t num_kv_heads, int32_t head_dim,
+                                       const int32_t* block_table, int32_t max_blocks_per_seq,
+                                       const int32_t* seq_lens, int32_t max_seq_len,
+                                       const float* k_scale, const float* v_scale,
+                                       float sm_scale, int32_t window, int32_t num_splits,
+                                       float* out, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  if (in_dtype != FA8_F32 && in_dtype != FA8_BF16)
+    return fail(FA8_EINVAL, "decode_append: in_dtype must be FA8_F32 or FA8_BF16");
+  if (batch > 0 && (!k_new || !v_new))
+    return fail(FA8_EINVAL, "decode_append: null k_new or v_new");
+  return decode_impl(q, batch, num_q_heads, cache, cache_dtype, num_blocks, num_kv_heads,
+                     head_dim, block_table, max_blocks_per_seq, seq_lens, max_seq_len, k_scale,
+                     v_scale, sm_scale, window, num_splits, out, workspace, workspace_bytes,
+                     stream, k_new, v_new, in_dtype);
 }
 
 int32_t fa8_prefill_kv_tile(int32_t head_dim) {

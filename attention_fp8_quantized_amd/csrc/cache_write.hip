@@ -18,33 +18,6 @@
 
 namespace fa8 {
 
-template <bool kInBf16>
-__device__ __forceinline__ void load_inputs(const void* src, int64_t elem, float* x,
-                                            int n) {
-  if constexpr (kInBf16) {
-    const uint4* p = reinterpret_cast<const uint4*>(
-        reinterpret_cast<const uint16_t*>(src) + elem);
-    for (int i = 0; i < n / 8; ++i) {
-      uint4 w = p[i];
-      uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-      for (int j = 0; j < 4; ++j) {
-        x[i * 8 + 2 * j] = bf16_lo(ws[j]);
-        x[i * 8 + 2 * j + 1] = bf16_hi(ws[j]);
-      }
-    }
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(
-        reinterpret_cast<const float*>(src) + elem);
-    for (int i = 0; i < n / 4; ++i) {
-      float4 w = p[i];
-      x[i * 4 + 0] = w.x;
-      x[i * 4 + 1] = w.y;
-      x[i * 4 + 2] = w.z;
-      x[i * 4 + 3] = w.w;
-    }
-  }
-}
-
 template <bool kInBf16, bool kFp8Cache>
 __global__ __launch_bounds__(256) void cache_write_kernel(
     const void* __restrict__ k, const void* __restrict__ v, int64_t n_tokens,
@@ -68,33 +41,15 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
     const int64_t slot = slot_mapping[n];
     if (slot < 0) continue;  // padding row
 
-    float x[kPerThread];
-    load_inputs<kInBf16>(src, (n * num_kv_heads + h) * head_dim + c * kPerThread,
-                         x, kPerThread);
-
-    uint32_t packed[4];
-    if constexpr (kFp8Cache) {
-      const float s = scale[h];
-      for (int w = 0; w < 4; ++w) {
-        uint32_t word = 0;
-        for (int j = 0; j < 4; ++j) {
-          const float y = x[w * 4 + j] / s;  // correctly rounded fp32 quotient
-          word |= e4m3_encode(y) << (8 * j);
-        }
-        packed[w] = word;
-      }
-    } else {
-      for (int w = 0; w < 4; ++w)
-        packed[w] = bf16_bits(x[2 * w]) | (bf16_bits(x[2 * w + 1]) << 16);
-    }
+    const uint4 chunk = encode_chunk<kInBf16, kFp8Cache>(
+        src, (n * num_kv_heads + h) * head_dim + c * kPerThread, kFp8Cache ? scale[h] : 1.0f);
 
     const int64_t blk = slot / kBlockSize;
     const int row = (int)(slot % kBlockSize);
     const int64_t off =
         ((((blk * num_kv_heads + h) * 2 + which) * kBlockSize + row) * head_dim +
          (int64_t)c * kPerThread) * kElemBytes;
-    *reinterpret_cast<uint4*>(cache + off) =
-        make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    *reinterpret_cast<uint4*>(cache + off) = chunk;
   }
 }
 

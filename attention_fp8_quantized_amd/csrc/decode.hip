@@ -304,7 +304,48 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFp8>())) void decode
     for (int hh = 0; hh < NL; ++hh) pg.v[hh] = *reinterpret_cast<const uint4*>(kb + HALF + 64 * hh);
   };
 
-  auto run_page = [&](const Page& pg, int page) {
+  // Fused append: the wave that will read the page holding token L-1 encodes
+  // that token's K and V row from the inputs (the same encoder as
+  // cache_write) before its page loop, stores it into the cache and into an
+  // LDS slot of its own, and swaps it in for the row the page load returns.
+  const bool append = p.k_new != nullptr && L > 0;
+  const int new_page = (L - 1) / kBlockSize;
+  const int new_row = (L - 1) % kBlockSize;
+  __shared__ __attribute__((aligned(16))) uint8_t s_new[2 * ROW];
+  const bool owner = append && new_page >= pg0 && new_page < pg1 && (new_page - pg0) % NW == wave;
+  if (owner && n == new_row) {
+    uint8_t* dst = const_cast<uint8_t*>(head_base) + (size_t)bt[new_page] * blk_stride;
+    const size_t src0 = ((size_t)b * p.num_kv_heads + h) * D;
+    const float ks = kFp8 ? p.k_scale[h] : 1.0f;
+    const float vs = kFp8 ? p.v_scale[h] : 1.0f;
+    for (int hh = 0; hh < NL; ++hh) {
+      const int e0 = kFp8 ? 64 * hh + 16 * g : 32 * hh + 8 * g;   // first element of the piece
+      uint4 kc, vc;
+      if (p.new_bf16) {
+        kc = encode_chunk<true, kFp8>(p.k_new, src0 + e0, ks);
+        vc = encode_chunk<true, kFp8>(p.v_new, src0 + e0, vs);
+      } else {
+        kc = encode_chunk<false, kFp8>(p.k_new, src0 + e0, ks);
+        vc = encode_chunk<false, kFp8>(p.v_new, src0 + e0, vs);
+      }
+      *reinterpret_cast<uint4*>(dst + 64 * hh) = kc;
+      *reinterpret_cast<uint4*>(dst + HALF + 64 * hh) = vc;
+      *reinterpret_cast<uint4*>(s_new + 64 * hh + 16 * g) = kc;
+      *reinterpret_cast<uint4*>(s_new + ROW + 64 * hh + 16 * g) = vc;
+    }
+  }
+  auto patch_new_row = [&](Page& pg) {
+    if (n != new_row) return;
+#pragma unroll
+    for (int hh = 0; hh < NL; ++hh) {
+      pg.k[hh] = *reinterpret_cast<const uint4*>(s_new + 64 * hh + 16 * g);
+      pg.v[hh] = *reinterpret_cast<const uint4*>(s_new + ROW + 64 * hh + 16 * g);
+    }
+  };
+
+  auto run_page = [&](const Page& pg_in, int page) {
+    Page pg = pg_in;
+    if (owner && page == new_page) patch_new_row(pg);
     // ---- S^T = K . Q^T ------------------------------------------------------
     f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll

@@ -111,6 +111,53 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// One 16-byte chunk of a cached row from its input elements (fp32 or bf16):
+// 16 e4m3 codes of fl32(x / scale) (correctly rounded quotient: callers are
+// built without fast-math and with correctly rounded division), or 8 bf16
+// values (scale unused).  `elem` indexes the input in elements.
+template <bool kInBf16, bool kFp8Cache>
+__device__ __forceinline__ uint4 encode_chunk(const void* src, int64_t elem, float scale) {
+  constexpr int N = kFp8Cache ? 16 : 8;
+  float x[N];
+  if constexpr (kInBf16) {
+    const uint4* ptr = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(src) + elem);
+#pragma unroll
+    for (int i = 0; i < N / 8; ++i) {
+      const uint4 w = ptr[i];
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[i * 8 + 2 * j] = bf16_lo(ws[j]);
+        x[i * 8 + 2 * j + 1] = bf16_hi(ws[j]);
+      }
+    }
+  } else {
+    const float4* ptr = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(src) + elem);
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      const float4 w = ptr[i];
+      x[i * 4 + 0] = w.x;
+      x[i * 4 + 1] = w.y;
+      x[i * 4 + 2] = w.z;
+      x[i * 4 + 3] = w.w;
+    }
+  }
+  uint32_t packed[4];
+  if constexpr (kFp8Cache) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) word |= e4m3_encode(x[w * 4 + j] / scale) << (8 * j);
+      packed[w] = word;
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) packed[w] = bf16_bits(x[2 * w]) | (bf16_bits(x[2 * w + 1]) << 16);
+  }
+  return make_uint4(packed[0], packed[1], packed[2], packed[3]);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);  // v_exp_f32; exp2(-inf) = 0
 }

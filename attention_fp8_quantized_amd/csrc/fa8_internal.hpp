@@ -30,6 +30,9 @@ struct DecodeParams {
   float* ws_m1;               // [B][Hq][NG]
   float* ws_l1;               // [B][Hq][NG]
   float* out;                 // [B][Hq][D]
+  const void* k_new;          // fused append: [B][Hkv][D] row of token seq_len-1 (or null)
+  const void* v_new;
+  int new_bf16;               // fused append input: bf16 (1) or fp32 (0)
   int batch, num_q_heads, num_kv_heads, head_dim, max_blocks;
   int num_splits, pages_per_split, window, fp8;
   int num_groups, group_size; // split groups merged first (1 group: single level)

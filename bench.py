@@ -4,8 +4,9 @@ Headline workload (one step): a Llama-3.1-8B-shaped decode step over 32
 distinct layers -- 32 query / 8 KV heads, head_dim 128, block size 16,
 batch 1, 32k-token context, K/V ~ N(0,1) with 1% outlier channels x20 and
 per-KV-head absmax/448 scales.  Per layer the step writes the current token's
-K/V into the FP8 cache (cache_write) and runs decode attention over the whole
-context.  The 32 layer caches (2.1 GB) are distinct, so the 256 MB
+K/V into the FP8 cache and runs decode attention over the whole context, in
+one launch (decode_attention_append); the same step as two launches
+(cache_write, then decode_attention) is reported beside it.  The 32 layer caches (2.1 GB) are distinct, so the 256 MB
 last-level cache cannot serve repeated reads.
 
 Printed: one JSON line with
@@ -221,6 +222,13 @@ class DecodeLayers:
         self.sm = 1.0 / math.sqrt(D)
         self.bytes_per_layer = decode_bytes(self.B, Hq, Hkv, D, self.lens, self.elem, window)
         self.write_bytes = cache_write_bytes(self.B, Hkv, D, 4, self.elem)
+
+    def run_layer_fused(self, i):
+        """The same step with one launch: the decode call writes the token."""
+        self.fa.decode_attention_append(self.qs[i], self.knew[i], self.vnew[i], self.cache,
+                                        self.bts[i], self.lens_dev, self.ks, self.vs, self.sm,
+                                        self.max_len, window=self.window, num_splits=self.S,
+                                        out=self.out, workspace=self.ws)
 
     def run_layer(self, i, write=True, events=None):
         fa = self.fa
@@ -507,6 +515,10 @@ def main():
 
     def step():
         for i in range(layers):
+            dl.run_layer_fused(i)
+
+    def step_two_launch():
+        for i in range(layers):
             dl.run_layer(i)
 
     def decode_launches():
@@ -537,6 +549,9 @@ def main():
     torch.cuda.synchronize()
     n_launch = args.steps * layers
     dec_ms = e0.elapsed_time(e1) / n_launch
+    # the same step as two launches per layer (cache_write, then decode)
+    two_ms = timed(torch, step_two_launch, args.steps)
+    log(f"two-launch step: {two_ms:.4f} ms")
 
     step_bytes = layers * (dl.bytes_per_layer + dl.write_bytes)
     value = step_bytes / (ms_step * 1e-3) / 1e9
@@ -561,6 +576,10 @@ def main():
         "dtype": "e4m3 cache, f32 math",
         "data": "synthetic: N(0,1) K/V with 1% outlier channels x20, absmax/448 per-KV-head "
                 "scales, device RNG",
+        "step": {"kernels": "decode_attention_append per layer (the current token's cache "
+                            "write fused into the decode launch)",
+                 "two_launch_ms_per_step": round(two_ms, 5),
+                 "two_launch_value": round(step_bytes / (two_ms * 1e-3) / 1e9, 2)},
         "config": {"workload": "Llama-3.1-8B-shaped FP8 decode step, 32 distinct layers",
                    "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
                    "block_size": 16, "context": ctx, "layers": layers, "splits": dl.S},

@@ -143,6 +143,35 @@ fa8_status fa8_decode_attention(const void* q, int32_t batch,
                                 void* stream);
 
 /*
+ * Fused decode step: write the current token's K/V into the cache and attend
+ * over the context including it, in one launch.  [BLOG] "Kernel 与 vLLM 改进"
+ * and "单请求 Benchmark": quantising the new token is a fixed per-step cost
+ * (the ITL intercept); here it rides on the decode launch instead of a
+ * separate cache-write launch.
+ *
+ * Same arguments and results as fa8_decode_attention, plus:
+ *   k_new, v_new  [batch][num_kv_heads][head_dim] rows of the current token
+ *                 (position seq_lens[b]-1 of each sequence), in_dtype FA8_F32
+ *                 or FA8_BF16.
+ *   cache         written: the row at slot
+ *                 block_table[b][(seq_lens[b]-1)/16]*16 + (seq_lens[b]-1)%16
+ *                 of each sequence with seq_lens[b] > 0 receives exactly the
+ *                 bytes fa8_cache_write would store for that row.
+ * The decode output equals running fa8_cache_write on those rows followed
+ * by fa8_decode_attention.
+ */
+fa8_status fa8_decode_attention_append(const void* q, const void* k_new, const void* v_new,
+                                       int32_t in_dtype, int32_t batch, int32_t num_q_heads,
+                                       void* cache, int32_t cache_dtype, int64_t num_blocks,
+                                       int32_t num_kv_heads, int32_t head_dim,
+                                       const int32_t* block_table, int32_t max_blocks_per_seq,
+                                       const int32_t* seq_lens, int32_t max_seq_len,
+                                       const float* k_scale, const float* v_scale,
+                                       float sm_scale, int32_t window, int32_t num_splits,
+                                       float* out, void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
+/*
  * Width (keys) of the KV tiles fa8_prefill_attention visits, in ascending,
  * tile-aligned order from key 0.  It is part of the numeric contract: the
  * probabilities are quantised to e4m3 against the running maximum reached

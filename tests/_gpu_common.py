@@ -62,7 +62,7 @@ class DecodeCase:
 
     def __init__(self, B, Hq, Hkv, D, lens, cache_dtype="e4m3", seed=0,
                  outliers=False, scales="absmax", window=0, oracle_heads=None,
-                 q_zero=False, fill=0):
+                 q_zero=False, fill=0, skip_last=False):
         import torch
         import attention_fp8_quantized_amd as fa
         self.B, self.Hq, self.Hkv, self.D = B, Hq, Hkv, D
@@ -97,9 +97,16 @@ class DecodeCase:
         # them (0xFF is a NaN code in e4m3 and a NaN half-word in bf16)
         self.cache = fa.new_cache(max(self.nblocks, 1), Hkv, D, cache_dtype)
         self.cache.view(torch.uint8).fill_(fill)
-        if N:
-            fa.cache_write(dev(k), dev(v), dev(self.slots), dev(self.ks), dev(self.vs),
-                           self.cache)
+        # skip_last: each sequence's last token stays unwritten (the current
+        # decode token, to be appended by the caller)
+        ends = np.cumsum(self.lens) - 1
+        self.last_idx = ends[self.lens > 0]
+        write = np.ones(N, dtype=bool)
+        if skip_last:
+            write[self.last_idx] = False
+        if write.any():
+            fa.cache_write(dev(k[write]), dev(v[write]), dev(self.slots[write]), dev(self.ks),
+                           dev(self.vs), self.cache)
         self.q_dev = qb.cuda()
         self.bt_dev = dev(self.bt)
         self.lens_dev = dev(self.lens)

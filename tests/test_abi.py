@@ -133,6 +133,27 @@ def test_decode_rejects_bad_arguments(lib):
     assert _decode(lib, B=0) == 0                            # empty batch: no-op
 
 
+def _decode_append(lib, **over):
+    fake = _p(0x1000)
+    a = dict(q=fake, kn=fake, vn=fake, idt=0, B=1, Hq=8, cache=fake, cd=2, nb=4, Hkv=2, D=64,
+             bt=fake, mb=4, lens=fake, maxlen=64, ks=fake, vs=fake, sm=0.125, window=0,
+             splits=1, out=fake, ws=_p(0x2000), wsb=1 << 20, stream=None)
+    a.update(over)
+    return lib.fa8_decode_attention_append(
+        a["q"], a["kn"], a["vn"], a["idt"], a["B"], a["Hq"], a["cache"], a["cd"], a["nb"],
+        a["Hkv"], a["D"], a["bt"], a["mb"], a["lens"], a["maxlen"], a["ks"], a["vs"], a["sm"],
+        a["window"], a["splits"], a["out"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_decode_append_rejects_bad_arguments(lib):
+    assert _decode_append(lib, idt=2) == EINVAL              # e4m3 is not an input type
+    assert _decode_append(lib, kn=None) == EINVAL
+    assert _decode_append(lib, vn=None) == EINVAL
+    assert _decode_append(lib, D=96) == EUNSUPPORTED         # decode checks still apply
+    assert _decode_append(lib, wsb=100) == EINVAL
+    assert _decode_append(lib, B=0, kn=None, vn=None) == 0   # empty batch: no-op
+
+
 def test_prefill_rejects_bad_arguments(lib):
     fake = _p(0x1000)
 

@@ -11,7 +11,7 @@ count).
 import numpy as np
 import pytest
 
-from _gpu_common import DecodeCase, assert_gate, log, metrics
+from _gpu_common import DecodeCase, assert_gate, dev, log, metrics
 
 pytestmark = pytest.mark.gpu
 
@@ -87,6 +87,46 @@ def test_stale_nan_rows_past_sequence_end(cd, window):
     c = DecodeCase(len(lens), 16, 2, 128, lens, cd, seed=33, window=window, fill=0xFF)
     got = _check(c, f"stale NaN rows {cd} window={window}")
     assert np.all(np.isfinite(got))
+
+
+@pytest.mark.parametrize("cd", ["e4m3", "bf16"])
+@pytest.mark.parametrize("in_dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("window", [0, 100])
+def test_fused_append_equals_write_then_decode(cd, in_dtype, window):
+    # the current token's K/V is written by the decode launch itself: the cache
+    # bytes and the output must equal cache_write followed by decode
+    import torch
+    import attention_fp8_quantized_amd as fa
+    lens = [300, 1, 17, 1000, 16, 0]
+    c = DecodeCase(len(lens), 16, 2, 128, lens, cd, seed=34, window=window, skip_last=True,
+                   fill=0xFF)
+    tdt = torch.bfloat16 if in_dtype == "bf16" else torch.float32
+    B, Hkv, D = c.B, c.Hkv, c.D
+    k_new = np.zeros((B, Hkv, D), np.float32)
+    v_new = np.zeros((B, Hkv, D), np.float32)
+    has = c.lens > 0
+    k_new[has] = c.k[c.last_idx]
+    v_new[has] = c.v[c.last_idx]
+    kd, vd = dev(k_new).to(tdt), dev(v_new).to(tdt)
+    start = c.cache.clone()
+    # write, then decode
+    sl = np.where(has, c.bt[np.arange(B), np.maximum(c.lens - 1, 0) // 16] * 16 +
+                  np.maximum(c.lens - 1, 0) % 16, -1).astype(np.int64)
+    fa.cache_write(kd, vd, dev(sl), c.ks_dev, c.vs_dev, c.cache)
+    ref_out = c.run_gpu()
+    ref_cache = c.cache.clone()
+    # fused
+    c.cache.copy_(start)
+    log(f"decode fused append {cd} in={in_dtype} window={window}")
+    out = fa.decode_attention_append(c.q_dev, kd, vd, c.cache, c.bt_dev, c.lens_dev, c.ks_dev,
+                                     c.vs_dev, float(c.sm), int(c.lens.max()), window=window)
+    torch.cuda.synchronize()
+    assert torch.equal(c.cache.view(torch.uint8), ref_cache.view(torch.uint8)), "cache bytes"
+    got = out.cpu().numpy()
+    np.testing.assert_array_equal(got, ref_out)
+    if in_dtype == "fp32":
+        ref, qheads = c.oracle()
+        assert_gate(got[:, qheads], ref, f"fused append {cd} window={window}")
 
 
 def test_page_permutation_invariance():
