@@ -95,3 +95,39 @@ def dequantize(codes, scale, cache_dtype):
         return np.float64(np.float32(scale)) * decode(codes)
     bits = np.asarray(codes, dtype=np.uint16).astype(np.uint32) << 16
     return bits.view(np.float32).astype(np.float64)
+
+
+E4M3_MAX = 448.0
+SCALE_FLOOR = np.float32(2.0 ** -126)   # smallest normal float32
+
+
+def absmax_scales(x, fmt_max=E4M3_MAX):
+    """Per-KV-head scales from the data itself: fl32(absmax_h / fmt_max).
+
+    [GPUSTACK] "キャリブレーション" (dynamic quantization: the value range is
+    computed at run time from the data), [EXPLAINER] "default scaleのまま本番へ
+    出さない" (a fixed, a dynamic or a calibrated scale), [BLOG] "Kernel and
+    vLLM improvements / Per-Head Scales" (one scale per KV head).  Readings:
+    the range is the largest magnitude, mapped onto the format's largest
+    finite value (448 for e4m3), so that value encodes to the top code
+    without saturating anything else.
+
+    x    float array [N][H_kv][D] (fp32 or bf16 values)
+    returns float32 [H_kv]:
+        absmax_h = max |x[n][h][d]| over the finite entries (NaN and +-inf
+                   are skipped; max over nothing is 0)
+        scale_h  = max(fl32(absmax_h / fmt_max), 2^-126)
+    The quotient is one correctly rounded float32 division; the floor keeps
+    an all-zero (or empty) head's scale positive and normal.
+    """
+    xf = np.asarray(x, dtype=np.float32)
+    if xf.ndim != 3:
+        raise ValueError("x must be [N][H_kv][D]")
+    a = np.abs(xf)
+    a = np.where(np.isfinite(a), a, np.float32(0.0))
+    if xf.shape[0] == 0:
+        amax = np.zeros(xf.shape[1], dtype=np.float32)
+    else:
+        amax = a.max(axis=(0, 2)).astype(np.float32)
+    q = np.divide(amax, np.float32(fmt_max), dtype=np.float32)
+    return np.maximum(q, SCALE_FLOOR).astype(np.float32)
