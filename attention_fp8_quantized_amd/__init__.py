@@ -16,7 +16,7 @@ import os
 
 __all__ = [
     "FA8_F32", "FA8_BF16", "FA8_E4M3", "BLOCK_SIZE", "Fa8Error", "library_path",
-    "load", "cache_write", "decode_num_splits", "decode_workspace_bytes",
+    "load", "cache_write", "absmax_scales", "decode_num_splits", "decode_workspace_bytes",
     "decode_attention", "decode_attention_append", "prefill_kv_tile", "prefill_attention",
     "new_cache",
     "new_decode_workspace",
@@ -44,6 +44,7 @@ _VP, _I32, _I64, _F32, _SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
 _SIGNATURES = {
     "fa8_cache_write": (_I32, [_VP, _VP, _I32, _I64, _I32, _I32, _VP, _VP, _VP, _VP,
                                _I32, _I64, _VP]),
+    "fa8_absmax_scales": (_I32, [_VP, _VP, _I32, _I64, _I32, _I32, _I32, _VP, _VP, _VP]),
     "fa8_decode_num_splits": (_I32, [_I32, _I32, _I32, _I32]),
     "fa8_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "fa8_decode_attention": (_I32, [_VP, _I32, _I32, _VP, _I32, _I64, _I32, _I32, _VP,
@@ -164,6 +165,36 @@ def cache_write(k, v, slot_mapping, k_scale, v_scale, cache):
         _ptr(k_scale) if cdt == FA8_E4M3 else None,
         _ptr(v_scale) if cdt == FA8_E4M3 else None,
         _ptr(cache), cdt, nb, _stream(cache)))
+
+
+def absmax_scales(k, v, k_scale=None, v_scale=None, cache_dtype="e4m3"):
+    """Per-KV-head scales of k/v [N][H_kv][D] (float32 or bfloat16) for an FP8
+    cache: max(fl32(absmax_h / 448), 2^-126) over the finite entries of head
+    h, computed on the device.  Writes into ``k_scale``/``v_scale`` (float32
+    [H_kv]) when given, else allocates them; returns (k_scale, v_scale)."""
+    torch = _torch()
+    _require(k, "k", ndim=3)
+    dev = k.device
+    _require(v, "v", dtype=k.dtype, device=dev, ndim=3)
+    if k.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("k/v must be float32 or bfloat16")
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    n, hkv, d = k.shape
+    if cache_dtype != "e4m3":
+        raise ValueError(f"no scales for cache_dtype {cache_dtype!r}")
+    out = []
+    for s, nm in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        if s is None:
+            s = torch.empty(hkv, dtype=torch.float32, device=dev)
+        _require(s, nm, dtype=torch.float32, device=dev, ndim=1)
+        if s.shape[0] != hkv:
+            raise ValueError(f"{nm} must have {hkv} entries")
+        out.append(s)
+    _check(load().fa8_absmax_scales(
+        _ptr(k), _ptr(v), FA8_BF16 if k.dtype == torch.bfloat16 else FA8_F32, n, hkv, d,
+        FA8_E4M3, _ptr(out[0]), _ptr(out[1]), _stream(k)))
+    return out[0], out[1]
 
 
 def decode_num_splits(batch, num_kv_heads, max_seq_len, window=0):

@@ -25,7 +25,8 @@ OUT = os.path.join(HERE, "libfa8attn.so")
 BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "cache_write.hip", "decode.hip", "prefill.hip", "stream_bench.hip"]
+SOURCES = ["api.hip", "cache_write.hip", "decode.hip", "prefill.hip", "scales.hip",
+           "stream_bench.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math",

@@ -108,6 +108,28 @@ fa8_status fa8_cache_write(const void* k, const void* v, int32_t in_dtype,
   return ok();
 }
 
+fa8_status fa8_absmax_scales(const void* k, const void* v, int32_t in_dtype,
+                             int64_t n_tokens, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t cache_dtype, float* k_scale, float* v_scale,
+                             void* stream) {
+  if (n_tokens < 0) return fail(FA8_EINVAL, "absmax_scales: n_tokens < 0");
+  if (in_dtype != FA8_F32 && in_dtype != FA8_BF16)
+    return fail(FA8_EINVAL, "absmax_scales: in_dtype must be FA8_F32 or FA8_BF16");
+  if (cache_dtype != FA8_E4M3)
+    return fail(FA8_EINVAL, "absmax_scales: cache_dtype must be an FP8 format");
+  if (num_kv_heads <= 0 || num_kv_heads > 4096)
+    return fail(FA8_EINVAL, "absmax_scales: num_kv_heads must be in 1..4096");
+  if (!head_dim_ok(head_dim))
+    return fail(FA8_EUNSUPPORTED, "absmax_scales: head_dim %d not in {64,128,256}", head_dim);
+  if (!k_scale || !v_scale) return fail(FA8_EINVAL, "absmax_scales: null k_scale or v_scale");
+  if (n_tokens > 0 && (!k || !v)) return fail(FA8_EINVAL, "absmax_scales: null k or v");
+  const hipError_t e = fa8::launch_absmax_scales(
+      k, v, in_dtype == FA8_BF16, n_tokens, num_kv_heads, head_dim, k_scale, v_scale, 448.0f,
+      device_cu_count(), reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "absmax_scales launch");
+  return ok();
+}
+
 int32_t fa8_decode_num_splits(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len,
                               int32_t window) {
   const int pages = decode_pages_max(max_seq_len, window);

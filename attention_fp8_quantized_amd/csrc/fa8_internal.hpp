@@ -14,6 +14,12 @@ hipError_t launch_cache_write(const void* k, const void* v, bool in_bf16,
                               const float* v_scale, void* cache, bool fp8_cache,
                               hipStream_t stream);
 
+// Per-KV-head absmax scales of k and v: three launches (zero, reduce,
+// finalize) that write only k_scale and v_scale.
+hipError_t launch_absmax_scales(const void* k, const void* v, bool in_bf16, int64_t n_tokens,
+                                int num_kv_heads, int head_dim, float* k_scale,
+                                float* v_scale, float fmt_max, int cus, hipStream_t stream);
+
 struct DecodeParams {
   const uint16_t* q;          // bf16 [B][Hq][D]
   const uint8_t* cache;       // [nb][Hkv][2][16][D] elements

@@ -118,7 +118,8 @@ def measured_traffic():
 def fill_pool(fa, torch, pool_blocks, Hkv, D, cache_dtype, seed, outliers=True):
     """A pool of blocks filled through the library's cache_write from
     N(0,1) K/V (seeded device RNG), optionally with 1% outlier channels x20,
-    and absmax/448 per-head scales over the pool.  Returns
+    and per-head scales max(absmax/448, 2^-126) over the pool computed by the
+    library's absmax_scales.  Returns
     (cache, k_scale, v_scale)."""
     dev = torch.device("cuda")
     cache = fa.new_cache(pool_blocks, Hkv, D, cache_dtype, device=dev)
@@ -133,17 +134,20 @@ def fill_pool(fa, torch, pool_blocks, Hkv, D, cache_dtype, seed, outliers=True):
     mul_k, mul_v = mul_k.view(1, Hkv, D), mul_v.view(1, Hkv, D)
     total = pool_blocks * 16
     chunk = 1 << 16
-    amax_k = torch.zeros(Hkv, device=dev)
+    amax_k = torch.zeros(Hkv, device=dev)   # becomes the per-head scales
     amax_v = torch.zeros(Hkv, device=dev)
     state = gen.get_state()
     for t0 in range(0, total, chunk):
         n = min(chunk, total - t0)
         k = torch.randn((n, Hkv, D), generator=gen, device=dev) * mul_k
         v = torch.randn((n, Hkv, D), generator=gen, device=dev) * mul_v
-        amax_k = torch.maximum(amax_k, k.abs().amax(dim=(0, 2)))
-        amax_v = torch.maximum(amax_v, v.abs().amax(dim=(0, 2)))
-    ks = (amax_k / 448.0).float().contiguous()
-    vs = (amax_v / 448.0).float().contiguous()
+        # the library's on-device scales of this chunk; the scale of the
+        # whole pool is the largest chunk scale (the quotient is monotone)
+        cks, cvs = fa.absmax_scales(k, v)
+        amax_k = torch.maximum(amax_k, cks)
+        amax_v = torch.maximum(amax_v, cvs)
+    ks = amax_k.contiguous()
+    vs = amax_v.contiguous()
     gen.set_state(state)
     for t0 in range(0, total, chunk):
         n = min(chunk, total - t0)
@@ -426,6 +430,31 @@ def measure_hd256(fa, torch, reps=3):
     return res
 
 
+def measure_absmax(fa, torch, reps=10):
+    """On-device per-KV-head scales over the rows of a 128k-token
+    Llama-shaped layer (131072 x 8 x 128 for k and for v), fp32 and bf16
+    rows.  HBM-bound: every input byte is read once."""
+    n, h, d = 131072, 8, 128
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(6000)
+    res = {}
+    for name, dt in (("f32", torch.float32), ("bf16", torch.bfloat16)):
+        k = torch.randn((n, h, d), generator=gen, device="cuda").to(dt)
+        v = torch.randn((n, h, d), generator=gen, device="cuda").to(dt)
+        ks = torch.empty(h, device="cuda")
+        vs = torch.empty(h, device="cuda")
+        ms = timed(torch, lambda: fa.absmax_scales(k, v, ks, vs), reps)
+        nbytes = 2 * k.numel() * k.element_size()
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"bytes": nbytes, "us": round(ms * 1e3, 2), "gbs": round(gbs, 1),
+                     "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        log(f"  absmax scales {name}: {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
+        del k, v
+    torch.cuda.empty_cache()
+    res["workload"] = "k and v rows of a 131072-token layer, 8 KV heads, head_dim 128"
+    return res
+
+
 def cpu_baseline(Hq, Hkv, D, ctx, budget_s=10.0):
     """The fp64 oracle decoding one Llama-shaped layer at ``ctx`` on the host
     (bounded sample: one layer, repeated until ``budget_s`` of CPU time)."""
@@ -607,6 +636,8 @@ def main():
         result["hybrid"] = measure_hybrid(fa, torch)
         log("head_dim 256")
         result["hd256"] = measure_hd256(fa, torch)
+        log("on-device absmax scales")
+        result["absmax_scales"] = measure_absmax(fa, torch)
         if not args.no_cpu:
             log("cpu baseline: oracle decode")
             result["cpu_baseline"] = cpu_baseline(Hq, Hkv, D, ctx)

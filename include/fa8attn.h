@@ -84,6 +84,35 @@ fa8_status fa8_cache_write(const void* k, const void* v, int32_t in_dtype,
                            void* stream);
 
 /*
+ * Per-KV-head scales computed on the device from the rows about to be
+ * cached (dynamic scales).  [GPUSTACK] "キャリブレーション" (dynamic
+ * quantization measures the value range at run time); [EXPLAINER]
+ * "default scaleのまま本番へ出さない" (a scale must fit the data: too small
+ * clips, too large wastes code points); [BLOG] "Kernel and vLLM improvements
+ * / Per-Head Scales" (one scale per KV head).
+ *
+ *   k, v          [n_tokens][num_kv_heads][head_dim], in_dtype FA8_F32 or
+ *                 FA8_BF16, row-major, contiguous (the same rows
+ *                 fa8_cache_write takes).
+ *   cache_dtype   FA8_E4M3: the largest finite code value, 448, is the
+ *                 target of each head's largest magnitude.
+ *   k_scale, v_scale  fp32 [num_kv_heads], written:
+ *       scale[h] = max(fl32(absmax_h / 448), 2^-126)
+ *   with absmax_h the largest |x| over all finite entries of head h (NaN
+ *   and +-inf are skipped; no rows or all zeros give the floor 2^-126) and
+ *   the fp32 quotient correctly rounded.  The result is exact: it does not
+ *   depend on the order in which the device combines partial maxima.
+ * Between the call's launches k_scale/v_scale hold intermediate bit
+ * patterns; they are final once the stream reaches the end of the call.
+ * k_scale and v_scale must not overlap k or v.  n_tokens == 0 writes the
+ * floor.  num_kv_heads is at most 4096.
+ */
+fa8_status fa8_absmax_scales(const void* k, const void* v, int32_t in_dtype,
+                             int64_t n_tokens, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t cache_dtype, float* k_scale, float* v_scale,
+                             void* stream);
+
+/*
  * Split-KV decode: number of context splits the library picks for a batch
  * (host-only heuristic; depends on the device's CU count).  `window` as in
  * fa8_decode_attention.  Always >= 1.

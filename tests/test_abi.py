@@ -172,3 +172,22 @@ def test_prefill_rejects_bad_arguments(lib):
     assert call(acc=2) == EINVAL
     assert call(qs=None) == EINVAL
     assert call(B=0) == 0
+
+
+def test_absmax_scales_rejects_bad_arguments(lib):
+    fake = _p(0x1000)
+
+    def call(**over):
+        a = dict(k=fake, v=fake, idt=0, n=4, H=2, D=64, cd=2, ks=fake, vs=fake)
+        a.update(over)
+        return lib.fa8_absmax_scales(a["k"], a["v"], a["idt"], a["n"], a["H"], a["D"], a["cd"],
+                                     a["ks"], a["vs"], None)
+
+    assert call(idt=2) == EINVAL                 # e4m3 is not an input type
+    assert call(cd=1) == EINVAL                  # a bf16 cache takes no scales
+    assert call(H=0) == EINVAL
+    assert call(H=4097) == EINVAL
+    assert call(D=96) == EUNSUPPORTED
+    assert call(ks=None) == EINVAL
+    assert call(k=None) == EINVAL
+    assert call(n=-1) == EINVAL
