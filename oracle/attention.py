@@ -46,8 +46,9 @@ def gather_kv(cache, block_table_row, lo, hi, head, cache_dtype, k_scale, v_scal
     rows = t % BLOCK_SIZE
     kc = cache[blocks, head, 0, rows, :]
     vc = cache[blocks, head, 1, rows, :]
-    ks = k_scale[head] if cache_dtype == "e4m3" else None
-    vs = v_scale[head] if cache_dtype == "e4m3" else None
+    fp8 = cache_dtype in ("e4m3", "e5m2")
+    ks = k_scale[head] if fp8 else None
+    vs = v_scale[head] if fp8 else None
     return dequantize(kc, ks, cache_dtype), dequantize(vc, vs, cache_dtype)
 
 
@@ -164,15 +165,16 @@ def quantize_query(q, q_scale):
 
 
 def _prefill_rows_pair(q, cu_q_lens, cache, block_table, seq_lens, q_scale, k_scale,
-                       v_scale, sm_scale, window, rows, row_fn):
+                       v_scale, sm_scale, window, rows, row_fn, cache_dtype="e4m3"):
     """Like _prefill_rows for a row function returning a [2][D] array."""
     out = _prefill_rows(q, cu_q_lens, cache, block_table, seq_lens, q_scale, k_scale,
-                        v_scale, sm_scale, window, rows, row_fn, width=2)
+                        v_scale, sm_scale, window, rows, row_fn, width=2,
+                        cache_dtype=cache_dtype)
     return out[:, :, 0, :].copy(), out[:, :, 1, :].copy()
 
 
 def _prefill_rows(q, cu_q_lens, cache, block_table, seq_lens, q_scale, k_scale,
-                  v_scale, sm_scale, window, rows, row_fn, width=None):
+                  v_scale, sm_scale, window, rows, row_fn, width=None, cache_dtype="e4m3"):
     q = np.asarray(q, dtype=np.float64)
     Ttot, Hq, D = q.shape
     Hkv = cache.shape[1]
@@ -195,7 +197,7 @@ def _prefill_rows(q, cu_q_lens, cache, block_table, seq_lens, q_scale, k_scale,
         lo_all = min(visible_range(int(p), window)[0] for p in pos)
         hi_all = int(pos.max()) + 1
         for h in range(Hkv):
-            K, V = gather_kv(cache, block_table[b], lo_all, hi_all, h, "e4m3",
+            K, V = gather_kv(cache, block_table[b], lo_all, hi_all, h, cache_dtype,
                              k_scale, v_scale)
             keys = np.arange(lo_all, hi_all)
             for g in range(G):
@@ -214,13 +216,16 @@ def _exact_row(s, keys, V):
 
 
 def prefill_exact(q, cu_q_lens, cache, block_table, seq_lens, q_scale, k_scale,
-                  v_scale, sm_scale, window, rows=None):
+                  v_scale, sm_scale, window, rows=None, cache_dtype="e4m3"):
     """Softmax attention with FP8-quantised Q, K, V and an unquantised P.
 
     ``rows`` selects packed query rows (default: all); returns [R][H_q][D].
-    Not the parity target of the GPU kernel (FP8 P is part of the method)."""
+    ``cache_dtype`` is the FP8 format of the cache ('e4m3' or 'e5m2'); the
+    query is always e4m3.  Not the parity target of the GPU kernel (FP8 P is
+    part of the method)."""
     return _prefill_rows(q, cu_q_lens, cache, block_table, seq_lens, q_scale,
-                         k_scale, v_scale, sm_scale, window, rows, _exact_row)
+                         k_scale, v_scale, sm_scale, window, rows, _exact_row,
+                         cache_dtype=cache_dtype)
 
 
 def mirror_row(s, keys, V, kv_tile, quantize_p=True, flip_tol=0.0, return_slack=False):
@@ -265,7 +270,7 @@ def mirror_row(s, keys, V, kv_tile, quantize_p=True, flip_tol=0.0, return_slack=
 
 def prefill_mirror(q, cu_q_lens, cache, block_table, seq_lens, q_scale, k_scale,
                    v_scale, sm_scale, window, kv_tile, rows=None, quantize_p=True,
-                   flip_tol=None):
+                   flip_tol=None, cache_dtype="e4m3"):
     """Tile-mirrored FP8-P reference (the parity target of the prefill kernel).
 
     ``kv_tile`` is the key-tile width the kernel visits (its value is part of
@@ -280,13 +285,15 @@ def prefill_mirror(q, cu_q_lens, cache, block_table, seq_lens, q_scale, k_scale,
     if flip_tol is None:
         fn = lambda s, keys, V: mirror_row(s, keys, V, kv_tile, quantize_p)  # noqa: E731
         return _prefill_rows(q, cu_q_lens, cache, block_table, seq_lens, q_scale,
-                             k_scale, v_scale, sm_scale, window, rows, fn)
+                             k_scale, v_scale, sm_scale, window, rows, fn,
+                             cache_dtype=cache_dtype)
     # With flip_tol: returns (out, slack), slack stacked after out along a
     # new leading axis of length 2 in the per-row function, split here.
     fn = lambda s, keys, V: np.stack(mirror_row(s, keys, V, kv_tile, quantize_p,  # noqa: E731
                                                 flip_tol, True))
     both = _prefill_rows_pair(q, cu_q_lens, cache, block_table, seq_lens, q_scale,
-                              k_scale, v_scale, sm_scale, window, rows, fn)
+                              k_scale, v_scale, sm_scale, window, rows, fn,
+                              cache_dtype=cache_dtype)
     return both[0], both[1]
 
 

@@ -17,23 +17,32 @@ slot ids are padding and write nothing.
 
 import numpy as np
 
+from . import e5m2
 from .e4m3 import encode, bf16_round
 
 BLOCK_SIZE = 16
 
 
-def quantize_rows(x, scale):
-    """e4m3 codes of fl32(fl32(x) / fl32(scale)) (scale broadcasts over x).
+FP8_CACHES = ("e4m3", "e5m2")
+
+
+def quantize_rows(x, scale, fmt="e4m3"):
+    """FP8 codes (``fmt`` e4m3 or e5m2) of fl32(fl32(x) / fl32(scale)) (scale
+    broadcasts over x).
 
     The quotient is one IEEE float32 division (correctly rounded); its result
     is then encoded with round-to-nearest-even and saturation.  The double
-    rounding (fp32 quotient, then e4m3) is part of the definition.
+    rounding (fp32 quotient, then FP8) is part of the definition.
     """
     xf = np.asarray(x, dtype=np.float32)
     sf = np.asarray(scale, dtype=np.float32)
     with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
         y = np.divide(xf, sf, dtype=np.float32)
-    return encode(y)
+    if fmt == "e4m3":
+        return encode(y)
+    if fmt == "e5m2":
+        return e5m2.encode(y)
+    raise ValueError(fmt)
 
 
 def bf16_bits(x):
@@ -43,9 +52,10 @@ def bf16_bits(x):
 
 
 def new_cache(num_blocks, num_kv_heads, head_dim, cache_dtype, fill=None):
-    """Host image of a paged cache: uint8 for 'e4m3', uint16 bits for 'bf16'."""
+    """Host image of a paged cache: uint8 codes for 'e4m3' and 'e5m2', uint16
+    bits for 'bf16'."""
     shape = (num_blocks, num_kv_heads, 2, BLOCK_SIZE, head_dim)
-    dt = np.uint8 if cache_dtype == "e4m3" else np.uint16
+    dt = np.uint8 if cache_dtype in FP8_CACHES else np.uint16
     c = np.zeros(shape, dtype=dt)
     if fill is not None:
         c[...] = fill
@@ -69,11 +79,11 @@ def cache_write(cache, k, v, slot_mapping, k_scale, v_scale, cache_dtype):
     row = slots[keep] % BLOCK_SIZE
     kk = k[keep]
     vv = v[keep]
-    if cache_dtype == "e4m3":
+    if cache_dtype in FP8_CACHES:
         ks = np.asarray(k_scale, dtype=np.float32)[None, :, None]
         vs = np.asarray(v_scale, dtype=np.float32)[None, :, None]
-        kc = quantize_rows(kk, ks)
-        vc = quantize_rows(vv, vs)
+        kc = quantize_rows(kk, ks, cache_dtype)
+        vc = quantize_rows(vv, vs, cache_dtype)
     elif cache_dtype == "bf16":
         kc = bf16_bits(kk)
         vc = bf16_bits(vv)
@@ -87,17 +97,20 @@ def cache_write(cache, k, v, slot_mapping, k_scale, v_scale, cache_dtype):
 
 
 def dequantize(codes, scale, cache_dtype):
-    """Dequantised values in float64: scale * decode(code) for e4m3 (exact:
-    a 24-bit scale times a 4-bit significand fits in 53 bits), or the bf16
-    value for the bf16 cache."""
+    """Dequantised values in float64: scale * decode(code) for e4m3 and e5m2
+    (exact: a 24-bit scale times a 4- or 3-bit significand fits in 53 bits),
+    or the bf16 value for the bf16 cache."""
     if cache_dtype == "e4m3":
         from .e4m3 import decode
         return np.float64(np.float32(scale)) * decode(codes)
+    if cache_dtype == "e5m2":
+        return np.float64(np.float32(scale)) * e5m2.decode(codes)
     bits = np.asarray(codes, dtype=np.uint16).astype(np.uint32) << 16
     return bits.view(np.float32).astype(np.float64)
 
 
 E4M3_MAX = 448.0
+E5M2_MAX = e5m2.E5M2_MAX
 SCALE_FLOOR = np.float32(2.0 ** -126)   # smallest normal float32
 
 
@@ -109,8 +122,8 @@ def absmax_scales(x, fmt_max=E4M3_MAX):
     出さない" (a fixed, a dynamic or a calibrated scale), [BLOG] "Kernel and
     vLLM improvements / Per-Head Scales" (one scale per KV head).  Readings:
     the range is the largest magnitude, mapped onto the format's largest
-    finite value (448 for e4m3), so that value encodes to the top code
-    without saturating anything else.
+    finite value (448 for e4m3, 57344 for e5m2), so that value encodes to the
+    top code without saturating anything else.
 
     x    float array [N][H_kv][D] (fp32 or bf16 values)
     returns float32 [H_kv]:

@@ -19,7 +19,7 @@ import pytest
 import workloads as W
 from oracle import attention as A
 from oracle import quant as Qn
-from oracle import e4m3
+from oracle import e4m3, e5m2
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -79,6 +79,31 @@ def test_cache_write_scale_divides():
     assert e4m3.decode(c2[0, 0, 1, 0, 0]) == 0.75     # 3 / 4
 
 
+def test_e5m2_cache_write_layout_and_scale():
+    Hkv, D = 2, 4
+    cache = Qn.new_cache(3, Hkv, D, "e5m2", fill=0xA5)
+    k = np.arange(2 * Hkv * D, dtype=np.float32).reshape(2, Hkv, D) * np.float32(1000.0)
+    v = -k
+    ks = np.array([0.5, 1.0], np.float32)
+    vs = np.array([4.0, 2.0], np.float32)
+    Qn.cache_write(cache, k, v, np.array([-1, 33]), ks, vs, "e5m2")
+    # slot 33 -> block 2, row 1;  the first row is padding (slot -1)
+    for h in range(Hkv):
+        for d in range(D):
+            assert cache[2, h, 0, 1, d] == e5m2.encode(np.float32(k[1, h, d] / ks[h]))
+            assert cache[2, h, 1, 1, d] == e5m2.encode(np.float32(-k[1, h, d] / vs[h]))
+    touched = np.zeros(cache.shape, dtype=bool)
+    touched[2, :, :, 1, :] = True
+    assert np.all(cache[~touched] == 0xA5)
+    # by hand: head 1, channel 3 holds 15000 / 1.0; the e5m2 grid in
+    # [8192, 16384) has step 2048, so the nearest value is 14336.  Head 0,
+    # channel 3 holds 11000 / 0.5 = 22000; step 4096 in [16384, 32768): 20480
+    assert e5m2.decode(cache[2, 1, 0, 1, 3]) == 14336.0
+    assert e5m2.decode(cache[2, 0, 0, 1, 3]) == 20480.0
+    # dequantisation multiplies back by the scale
+    assert Qn.dequantize(cache[2, 0, 0, 1, 3], ks[0], "e5m2") == 10240.0
+
+
 def test_bf16_cache_ignores_scales():
     g = np.random.default_rng(1)
     k = g.standard_normal((3, 2, 8)).astype(np.float32)
@@ -109,9 +134,10 @@ def _literal_decode(q, cache, bt, lens, ks, vs, sm, window, Hkv, cd):
             for t in range(lo, L):
                 blk = int(bt[b][t // 16])
                 row = t % 16
-                if cd == "e4m3":
-                    kv = [float(ks[h]) * e4m3.decode_code(int(cache[blk, h, 0, row, d])) for d in range(D)]
-                    vv = [float(vs[h]) * e4m3.decode_code(int(cache[blk, h, 1, row, d])) for d in range(D)]
+                if cd in ("e4m3", "e5m2"):
+                    dc = e4m3.decode_code if cd == "e4m3" else e5m2.decode_code
+                    kv = [float(ks[h]) * dc(int(cache[blk, h, 0, row, d])) for d in range(D)]
+                    vv = [float(vs[h]) * dc(int(cache[blk, h, 1, row, d])) for d in range(D)]
                 else:
                     kv = [float(np.uint32(int(cache[blk, h, 0, row, d]) << 16).view(np.float32)) for d in range(D)]
                     vv = [float(np.uint32(int(cache[blk, h, 1, row, d]) << 16).view(np.float32)) for d in range(D)]
@@ -130,7 +156,7 @@ def _literal_decode(q, cache, bt, lens, ks, vs, sm, window, Hkv, cd):
     return out
 
 
-@pytest.mark.parametrize("cd", ["e4m3", "bf16"])
+@pytest.mark.parametrize("cd", ["e4m3", "e5m2", "bf16"])
 @pytest.mark.parametrize("window", [0, 7])
 def test_decode_vs_literal_loop(cd, window):
     c = _case(B=2, Hq=4, Hkv=2, D=8, lens=(37, 5), cache_dtype=cd, seed=3)
