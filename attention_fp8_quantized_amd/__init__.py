@@ -1,4 +1,5 @@
-"""Python binding of libfa8attn.so (FP8-e4m3 paged-KV attention for gfx950).
+"""Python binding of libfa8attn.so (FP8 paged-KV attention for gfx950: e4m3 or
+e5m2 cache codes with per-KV-head scales, or a bf16 cache).
 
 Argument marshalling only: every step runs in the library's HIP kernels.
 torch supplies device memory (``data_ptr``) and the stream
@@ -7,22 +8,24 @@ If the library is missing the import of this module still works, but every
 call raises ``RuntimeError`` (there is no fallback path).
 
 Names follow the C ABI in include/fa8attn.h:
-    cache_write, decode_num_splits, decode_workspace_bytes,
-    decode_attention, prefill_kv_tile, prefill_attention
+    cache_write, absmax_scales, decode_num_splits, decode_workspace_bytes,
+    decode_attention, decode_attention_append, prefill_kv_tile,
+    prefill_attention, stream_read, stream_copy
 """
 
 import ctypes
 import os
 
 __all__ = [
-    "FA8_F32", "FA8_BF16", "FA8_E4M3", "BLOCK_SIZE", "Fa8Error", "library_path",
+    "FA8_F32", "FA8_BF16", "FA8_E4M3", "FA8_E5M2", "BLOCK_SIZE", "Fa8Error", "library_path",
     "load", "cache_write", "absmax_scales", "decode_num_splits", "decode_workspace_bytes",
     "decode_attention", "decode_attention_append", "prefill_kv_tile", "prefill_attention",
     "new_cache",
     "new_decode_workspace",
 ]
 
-FA8_F32, FA8_BF16, FA8_E4M3 = 0, 1, 2
+FA8_F32, FA8_BF16, FA8_E4M3, FA8_E5M2 = 0, 1, 2, 3
+_FP8 = (FA8_E4M3, FA8_E5M2)
 BLOCK_SIZE = 16
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -54,7 +57,7 @@ _SIGNATURES = {
                                             _I32, _I32, _VP, _I32, _VP, _I32, _VP, _VP, _F32,
                                             _I32, _I32, _VP, _VP, _SZ, _VP]),
     "fa8_prefill_kv_tile": (_I32, [_I32]),
-    "fa8_prefill_attention": (_I32, [_VP, _VP, _I32, _I32, _I32, _VP, _I64, _I32, _I32,
+    "fa8_prefill_attention": (_I32, [_VP, _VP, _I32, _I32, _I32, _VP, _I32, _I64, _I32, _I32,
                                      _VP, _I32, _VP, _VP, _VP, _VP, _F32, _I32, _I32,
                                      _VP, _VP]),
     "fa8_stream_read": (_I32, [_VP, _SZ, _VP, _VP]),
@@ -118,24 +121,34 @@ def _require(t, name, dtype=None, device=None, ndim=None):
 
 
 def _cache_dtype(cache):
+    """fa8_dtype of a cache tensor: uint8 or float8_e4m3fn holds e4m3 codes,
+    float8_e5m2 e5m2 codes, bfloat16 (or 16-bit integers) bf16 values."""
     torch = _torch()
-    if cache.dtype == torch.uint8:
+    if cache.dtype in (torch.uint8, torch.float8_e4m3fn):
         return FA8_E4M3
+    if cache.dtype == torch.float8_e5m2:
+        return FA8_E5M2
     if cache.dtype in (torch.bfloat16, torch.int16, torch.uint16):
         return FA8_BF16
-    raise ValueError("cache must be uint8 (e4m3 codes) or bfloat16")
+    raise ValueError("cache must be uint8 / float8_e4m3fn (e4m3 codes), float8_e5m2 "
+                     "(e5m2 codes) or bfloat16")
 
 
 def new_cache(num_blocks, num_kv_heads, head_dim, cache_dtype="e4m3", device="cuda"):
-    """Allocate a paged cache tensor [num_blocks][H_kv][2][16][head_dim]."""
+    """Allocate a paged cache tensor [num_blocks][H_kv][2][16][head_dim]:
+    uint8 codes for 'e4m3', float8_e5m2 codes for 'e5m2', bfloat16 for
+    'bf16'."""
     torch = _torch()
-    dt = torch.uint8 if cache_dtype == "e4m3" else torch.bfloat16
+    dts = {"e4m3": torch.uint8, "e5m2": torch.float8_e5m2, "bf16": torch.bfloat16}
+    if cache_dtype not in dts:
+        raise ValueError(f"cache_dtype must be one of {sorted(dts)}")
+    dt = dts[cache_dtype]
     return torch.empty((num_blocks, num_kv_heads, 2, BLOCK_SIZE, head_dim),
                        dtype=dt, device=device)
 
 
 def cache_write(k, v, slot_mapping, k_scale, v_scale, cache):
-    """Quantise (e4m3 cache) or round (bf16 cache) k/v [N][H_kv][D] into the
+    """Quantise (FP8 cache) or round (bf16 cache) k/v [N][H_kv][D] into the
     paged cache at ``slot_mapping`` (int64 [N]; negative = skip)."""
     torch = _torch()
     _require(cache, "cache", ndim=5)
@@ -153,7 +166,7 @@ def cache_write(k, v, slot_mapping, k_scale, v_scale, cache):
     if slot_mapping.shape[0] != k.shape[0]:
         raise ValueError("slot_mapping must have one entry per row")
     cdt = _cache_dtype(cache)
-    if cdt == FA8_E4M3:
+    if cdt in _FP8:
         for s, nm in ((k_scale, "k_scale"), (v_scale, "v_scale")):
             _require(s, nm, dtype=torch.float32, device=dev, ndim=1)
             if s.shape[0] != hkv:
@@ -162,15 +175,15 @@ def cache_write(k, v, slot_mapping, k_scale, v_scale, cache):
     _check(lib.fa8_cache_write(
         _ptr(k), _ptr(v), FA8_BF16 if k.dtype == torch.bfloat16 else FA8_F32,
         k.shape[0], hkv, d, _ptr(slot_mapping),
-        _ptr(k_scale) if cdt == FA8_E4M3 else None,
-        _ptr(v_scale) if cdt == FA8_E4M3 else None,
+        _ptr(k_scale) if cdt in _FP8 else None,
+        _ptr(v_scale) if cdt in _FP8 else None,
         _ptr(cache), cdt, nb, _stream(cache)))
 
 
 def absmax_scales(k, v, k_scale=None, v_scale=None, cache_dtype="e4m3"):
     """Per-KV-head scales of k/v [N][H_kv][D] (float32 or bfloat16) for an FP8
-    cache: max(fl32(absmax_h / 448), 2^-126) over the finite entries of head
-    h, computed on the device.  Writes into ``k_scale``/``v_scale`` (float32
+    cache: max(fl32(absmax_h / F), 2^-126) over the finite entries of head
+    h, F = 448 ('e4m3') or 57344 ('e5m2'), computed on the device.  Writes into ``k_scale``/``v_scale`` (float32
     [H_kv]) when given, else allocates them; returns (k_scale, v_scale)."""
     torch = _torch()
     _require(k, "k", ndim=3)
@@ -181,7 +194,8 @@ def absmax_scales(k, v, k_scale=None, v_scale=None, cache_dtype="e4m3"):
     if k.shape != v.shape:
         raise ValueError("k and v must have the same shape")
     n, hkv, d = k.shape
-    if cache_dtype != "e4m3":
+    fmts = {"e4m3": FA8_E4M3, "e5m2": FA8_E5M2}
+    if cache_dtype not in fmts:
         raise ValueError(f"no scales for cache_dtype {cache_dtype!r}")
     out = []
     for s, nm in ((k_scale, "k_scale"), (v_scale, "v_scale")):
@@ -193,7 +207,7 @@ def absmax_scales(k, v, k_scale=None, v_scale=None, cache_dtype="e4m3"):
         out.append(s)
     _check(load().fa8_absmax_scales(
         _ptr(k), _ptr(v), FA8_BF16 if k.dtype == torch.bfloat16 else FA8_F32, n, hkv, d,
-        FA8_E4M3, _ptr(out[0]), _ptr(out[1]), _stream(k)))
+        fmts[cache_dtype], _ptr(out[0]), _ptr(out[1]), _stream(k)))
     return out[0], out[1]
 
 
@@ -227,7 +241,7 @@ def _decode_args(q, cache, block_table, seq_lens, k_scale, v_scale, max_seq_len,
     if block_table.shape[0] != B or seq_lens.shape[0] != B:
         raise ValueError("block_table / seq_lens must have one row per sequence")
     cdt = _cache_dtype(cache)
-    if cdt == FA8_E4M3:
+    if cdt in _FP8:
         _require(k_scale, "k_scale", dtype=torch.float32, device=dev, ndim=1)
         _require(v_scale, "v_scale", dtype=torch.float32, device=dev, ndim=1)
     splits = num_splits or decode_num_splits(B, hkv, int(max_seq_len), int(window))
@@ -243,8 +257,8 @@ def _decode_args(q, cache, block_table, seq_lens, k_scale, v_scale, max_seq_len,
     head = (_ptr(q),)
     tail = (B, hq, _ptr(cache), cdt, nb, hkv, d, _ptr(block_table), block_table.shape[1],
             _ptr(seq_lens), int(max_seq_len),
-            _ptr(k_scale) if cdt == FA8_E4M3 else None,
-            _ptr(v_scale) if cdt == FA8_E4M3 else None)
+            _ptr(k_scale) if cdt in _FP8 else None,
+            _ptr(v_scale) if cdt in _FP8 else None)
     return head, tail, splits, out, workspace
 
 
@@ -302,7 +316,10 @@ def prefill_attention(q, cu_q_lens, cache, block_table, seq_lens, q_scale, k_sca
     out fp32 [T][H_q][D].  ``seq_lens`` count the context including the
     chunk; ``q_scale`` is a 1-element fp32 device tensor."""
     torch = _torch()
-    _require(cache, "cache", dtype=torch.uint8, ndim=5)
+    _require(cache, "cache", ndim=5)
+    cdt = _cache_dtype(cache)
+    if cdt not in _FP8:
+        raise ValueError("prefill needs an FP8 (e4m3 or e5m2) cache")
     dev = cache.device
     nb, hkv, _, _, d = cache.shape
     _require(q, "q", dtype=torch.bfloat16, device=dev, ndim=3)
@@ -321,7 +338,7 @@ def prefill_attention(q, cu_q_lens, cache, block_table, seq_lens, q_scale, k_sca
         _require(out, "out", dtype=torch.float32, device=dev, ndim=3)
     lib = load()
     _check(lib.fa8_prefill_attention(
-        _ptr(q), _ptr(cu_q_lens), B, hq, int(max_q_len), _ptr(cache), nb, hkv, d,
+        _ptr(q), _ptr(cu_q_lens), B, hq, int(max_q_len), _ptr(cache), cdt, nb, hkv, d,
         _ptr(block_table), block_table.shape[1], _ptr(seq_lens), _ptr(q_scale),
         _ptr(k_scale), _ptr(v_scale), float(sm_scale), int(window), int(accum_mode),
         _ptr(out), _stream(cache)))

@@ -36,6 +36,12 @@ fa8_status hip_fail(hipError_t e, const char* what) {
 }
 
 bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
+bool fp8_cache(int32_t dt) { return dt == FA8_E4M3 || dt == FA8_E5M2; }
+
+// fa8_dtype of a cache -> kernel template format (caller checked the value)
+int kernel_fmt(int32_t dt) {
+  return dt == FA8_E4M3 ? fa8::kFmtE4m3 : dt == FA8_E5M2 ? fa8::kFmtE5m2 : fa8::kFmtBf16;
+}
 bool group_ok(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
 
 int device_cu_count() {
@@ -89,8 +95,8 @@ fa8_status fa8_cache_write(const void* k, const void* v, int32_t in_dtype,
   if (n_tokens < 0) return fail(FA8_EINVAL, "cache_write: n_tokens < 0");
   if (in_dtype != FA8_F32 && in_dtype != FA8_BF16)
     return fail(FA8_EINVAL, "cache_write: in_dtype must be FA8_F32 or FA8_BF16");
-  if (cache_dtype != FA8_E4M3 && cache_dtype != FA8_BF16)
-    return fail(FA8_EINVAL, "cache_write: cache_dtype must be FA8_E4M3 or FA8_BF16");
+  if (!fp8_cache(cache_dtype) && cache_dtype != FA8_BF16)
+    return fail(FA8_EINVAL, "cache_write: cache_dtype must be FA8_E4M3, FA8_E5M2 or FA8_BF16");
   if (num_kv_heads <= 0) return fail(FA8_EINVAL, "cache_write: num_kv_heads must be > 0");
   if (!head_dim_ok(head_dim))
     return fail(FA8_EUNSUPPORTED, "cache_write: head_dim %d not in {64,128,256}", head_dim);
@@ -98,11 +104,11 @@ fa8_status fa8_cache_write(const void* k, const void* v, int32_t in_dtype,
   if (n_tokens == 0) return ok();
   if (!k || !v || !slot_mapping || !cache)
     return fail(FA8_EINVAL, "cache_write: null k, v, slot_mapping or cache");
-  if (cache_dtype == FA8_E4M3 && (!k_scale || !v_scale))
-    return fail(FA8_EINVAL, "cache_write: FA8_E4M3 cache needs k_scale and v_scale");
+  if (fp8_cache(cache_dtype) && (!k_scale || !v_scale))
+    return fail(FA8_EINVAL, "cache_write: an FP8 cache needs k_scale and v_scale");
   const hipError_t e = fa8::launch_cache_write(
       k, v, in_dtype == FA8_BF16, n_tokens, num_kv_heads, head_dim, slot_mapping,
-      k_scale, v_scale, cache, cache_dtype == FA8_E4M3,
+      k_scale, v_scale, cache, kernel_fmt(cache_dtype),
       reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "cache_write launch");
   return ok();
@@ -115,8 +121,8 @@ fa8_status fa8_absmax_scales(const void* k, const void* v, int32_t in_dtype,
   if (n_tokens < 0) return fail(FA8_EINVAL, "absmax_scales: n_tokens < 0");
   if (in_dtype != FA8_F32 && in_dtype != FA8_BF16)
     return fail(FA8_EINVAL, "absmax_scales: in_dtype must be FA8_F32 or FA8_BF16");
-  if (cache_dtype != FA8_E4M3)
-    return fail(FA8_EINVAL, "absmax_scales: cache_dtype must be an FP8 format");
+  if (!fp8_cache(cache_dtype))
+    return fail(FA8_EINVAL, "absmax_scales: cache_dtype must be FA8_E4M3 or FA8_E5M2");
   if (num_kv_heads <= 0 || num_kv_heads > 4096)
     return fail(FA8_EINVAL, "absmax_scales: num_kv_heads must be in 1..4096");
   if (!head_dim_ok(head_dim))
@@ -124,7 +130,8 @@ fa8_status fa8_absmax_scales(const void* k, const void* v, int32_t in_dtype,
   if (!k_scale || !v_scale) return fail(FA8_EINVAL, "absmax_scales: null k_scale or v_scale");
   if (n_tokens > 0 && (!k || !v)) return fail(FA8_EINVAL, "absmax_scales: null k or v");
   const hipError_t e = fa8::launch_absmax_scales(
-      k, v, in_dtype == FA8_BF16, n_tokens, num_kv_heads, head_dim, k_scale, v_scale, 448.0f,
+      k, v, in_dtype == FA8_BF16, n_tokens, num_kv_heads, head_dim, k_scale, v_scale,
+      cache_dtype == FA8_E4M3 ? 448.0f : 57344.0f,
       device_cu_count(), reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "absmax_scales launch");
   return ok();
@@ -173,8 +180,8 @@ static fa8_status decode_impl(const void* q, int32_t batch, int32_t num_q_heads,
                 num_q_heads / num_kv_heads);
   if (!head_dim_ok(head_dim))
     return fail(FA8_EUNSUPPORTED, "decode: head_dim %d not in {64,128,256}", head_dim);
-  if (cache_dtype != FA8_E4M3 && cache_dtype != FA8_BF16)
-    return fail(FA8_EINVAL, "decode: cache_dtype must be FA8_E4M3 or FA8_BF16");
+  if (!fp8_cache(cache_dtype) && cache_dtype != FA8_BF16)
+    return fail(FA8_EINVAL, "decode: cache_dtype must be FA8_E4M3, FA8_E5M2 or FA8_BF16");
   if (max_seq_len < 0 || max_blocks_per_seq < 0 || num_blocks < 0)
     return fail(FA8_EINVAL, "decode: negative size");
   if ((int64_t)max_blocks_per_seq * FA8_BLOCK_SIZE < max_seq_len)
@@ -186,8 +193,8 @@ static fa8_status decode_impl(const void* q, int32_t batch, int32_t num_q_heads,
   if (batch == 0) return ok();
   if (!q || !cache || !block_table || !seq_lens || !out || !workspace)
     return fail(FA8_EINVAL, "decode: null pointer argument");
-  if (cache_dtype == FA8_E4M3 && (!k_scale || !v_scale))
-    return fail(FA8_EINVAL, "decode: FA8_E4M3 cache needs k_scale and v_scale");
+  if (fp8_cache(cache_dtype) && (!k_scale || !v_scale))
+    return fail(FA8_EINVAL, "decode: an FP8 cache needs k_scale and v_scale");
   if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
     return fail(FA8_EINVAL, "decode: workspace must be 16-byte aligned");
 
@@ -218,13 +225,13 @@ static fa8_status decode_impl(const void* q, int32_t batch, int32_t num_q_heads,
   const int pages = decode_pages_max(max_seq_len, window);
   p.pages_per_split = pages > 0 ? (pages + S - 1) / S : 1;
   p.window = window > 0 ? window : 0;
-  p.fp8 = cache_dtype == FA8_E4M3 ? 1 : 0;
+  p.fp8 = fp8_cache(cache_dtype) ? 1 : 0;
   p.sm_scale = sm_scale;
   p.k_new = k_new;
   p.v_new = v_new;
   p.new_bf16 = new_dtype == FA8_BF16 ? 1 : 0;
   const hipError_t e =
-      fa8::launch_decode(p, cache_dtype == FA8_E4M3, reinterpret_cast<hipStream_t>(stream));
+      fa8::launch_decode(p, kernel_fmt(cache_dtype), reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
 }
@@ -270,7 +277,8 @@ int32_t fa8_prefill_kv_tile(int32_t head_dim) {
 
 fa8_status fa8_prefill_attention(const void* q, const int32_t* cu_q_lens, int32_t batch,
                                  int32_t num_q_heads, int32_t max_q_len, const void* cache,
-                                 int64_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t cache_dtype, int64_t num_blocks,
+                                 int32_t num_kv_heads, int32_t head_dim,
                                  const int32_t* block_table, int32_t max_blocks_per_seq,
                                  const int32_t* seq_lens, const float* q_scale,
                                  const float* k_scale, const float* v_scale, float sm_scale,
@@ -285,6 +293,8 @@ fa8_status fa8_prefill_attention(const void* q, const int32_t* cu_q_lens, int32_
                 num_q_heads, num_kv_heads);
   if (!head_dim_ok(head_dim))
     return fail(FA8_EUNSUPPORTED, "prefill: head_dim %d not in {64,128,256}", head_dim);
+  if (!fp8_cache(cache_dtype))
+    return fail(FA8_EINVAL, "prefill: cache_dtype must be FA8_E4M3 or FA8_E5M2");
   if (accum_mode != 0 && accum_mode != 1)
     return fail(FA8_EINVAL, "prefill: accum_mode must be 0 or 1");
   if (!(std::isfinite(sm_scale)))
@@ -312,6 +322,7 @@ fa8_status fa8_prefill_attention(const void* q, const int32_t* cu_q_lens, int32_
   p.max_q_len = max_q_len;
   p.window = window > 0 ? window : 0;
   p.accum_mode = accum_mode;
+  p.fmt = kernel_fmt(cache_dtype);
   p.sm_scale = sm_scale;
   const hipError_t e = fa8::launch_prefill(p, reinterpret_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported)

@@ -1,12 +1,13 @@
 // Cache write: quantise new K/V rows with their per-KV-head scale and scatter
-// them into 16-token pages.
+// them into 16-token pages (e4m3 or e5m2 codes, or bf16 values).
 //
 // [BLOG] "Kernel and vLLM improvements / Per-Head Scales": the cache-write
 // kernel takes an array of scales, one per KV head.  [EXPLAINER] "FP8
 // combines value and scale": the value is divided by its scale before it is
-// quantised.  Rounding is nearest-even with saturation at +-448.
+// quantised.  Rounding is nearest-even with saturation at the format's largest
+// finite value (448 for e4m3, 57344 for e5m2).
 //
-// One thread produces one 16-byte chunk of one cached row: 16 e4m3 codes or
+// One thread produces one 16-byte chunk of one cached row: 16 FP8 codes or
 // 8 bf16 values.  Threads of a block walk (token, head, chunk) with the chunk
 // fastest, so input reads are contiguous; blockIdx.y picks K (0) or V (1).
 // The work is a single HBM-bound pass.  The fp32 quotient x / scale must be
@@ -18,12 +19,13 @@
 
 namespace fa8 {
 
-template <bool kInBf16, bool kFp8Cache>
+template <bool kInBf16, int kFmt>
 __global__ __launch_bounds__(256) void cache_write_kernel(
     const void* __restrict__ k, const void* __restrict__ v, int64_t n_tokens,
     int num_kv_heads, int head_dim, const int64_t* __restrict__ slot_mapping,
     const float* __restrict__ k_scale, const float* __restrict__ v_scale,
     uint8_t* __restrict__ cache) {
+  constexpr bool kFp8Cache = kFmt != kFmtBf16;
   constexpr int kElemBytes = kFp8Cache ? 1 : 2;
   constexpr int kPerThread = 16 / kElemBytes;  // elements per 16-byte chunk
   const int chunks_per_row = head_dim / kPerThread;
@@ -41,7 +43,7 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
     const int64_t slot = slot_mapping[n];
     if (slot < 0) continue;  // padding row
 
-    const uint4 chunk = encode_chunk<kInBf16, kFp8Cache>(
+    const uint4 chunk = encode_chunk<kInBf16, kFmt>(
         src, (n * num_kv_heads + h) * head_dim + c * kPerThread, kFp8Cache ? scale[h] : 1.0f);
 
     const int64_t blk = slot / kBlockSize;
@@ -56,34 +58,25 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
 hipError_t launch_cache_write(const void* k, const void* v, bool in_bf16,
                               int64_t n_tokens, int num_kv_heads, int head_dim,
                               const int64_t* slot_mapping, const float* k_scale,
-                              const float* v_scale, void* cache, bool fp8_cache,
+                              const float* v_scale, void* cache, int fmt,
                               hipStream_t stream) {
-  const int per = fp8_cache ? 16 : 8;
+  const int per = fmt != kFmtBf16 ? 16 : 8;
   const int64_t total = n_tokens * num_kv_heads * (head_dim / per);
   const int threads = 256;
   int64_t blocks = (total + threads - 1) / threads;
   if (blocks > 65535) blocks = 65535;  // grid-stride loop covers the rest
   dim3 grid((unsigned)blocks, 2);
   uint8_t* c = reinterpret_cast<uint8_t*>(cache);
-  if (fp8_cache) {
-    if (in_bf16)
-      hipLaunchKernelGGL((cache_write_kernel<true, true>), grid, threads, 0, stream,
-                         k, v, n_tokens, num_kv_heads, head_dim, slot_mapping,
-                         k_scale, v_scale, c);
-    else
-      hipLaunchKernelGGL((cache_write_kernel<false, true>), grid, threads, 0, stream,
-                         k, v, n_tokens, num_kv_heads, head_dim, slot_mapping,
-                         k_scale, v_scale, c);
-  } else {
-    if (in_bf16)
-      hipLaunchKernelGGL((cache_write_kernel<true, false>), grid, threads, 0, stream,
-                         k, v, n_tokens, num_kv_heads, head_dim, slot_mapping,
-                         k_scale, v_scale, c);
-    else
-      hipLaunchKernelGGL((cache_write_kernel<false, false>), grid, threads, 0, stream,
-                         k, v, n_tokens, num_kv_heads, head_dim, slot_mapping,
-                         k_scale, v_scale, c);
+#define FA8_CW(BF, FMT)                                                                     \
+  hipLaunchKernelGGL((cache_write_kernel<BF, FMT>), grid, threads, 0, stream, k, v, n_tokens, \
+                     num_kv_heads, head_dim, slot_mapping, k_scale, v_scale, c)
+  switch (fmt) {
+    case kFmtE4m3: if (in_bf16) FA8_CW(true, kFmtE4m3); else FA8_CW(false, kFmtE4m3); break;
+    case kFmtE5m2: if (in_bf16) FA8_CW(true, kFmtE5m2); else FA8_CW(false, kFmtE5m2); break;
+    case kFmtBf16: if (in_bf16) FA8_CW(true, kFmtBf16); else FA8_CW(false, kFmtBf16); break;
+    default: return hipErrorInvalidValue;
   }
+#undef FA8_CW
   return hipGetLastError();
 }
 

@@ -1,5 +1,5 @@
-// Split-KV decode over the paged FP8 / BF16 cache, with the cross-split
-// log-sum-exp merge fused into the same launch.
+// Split-KV decode over the paged FP8 (e4m3 or e5m2) / BF16 cache, with the
+// cross-split log-sum-exp merge fused into the same launch.
 //
 // [BLOG] "性能 Benchmark / 单请求 Benchmark" (single-request benchmark):
 // decode time is the per-token read of the cache, which the FP8 cache halves;
@@ -27,7 +27,7 @@
 //     keys 4g..4g+3 for query head n;
 //   * softmax in the log2 domain: page maximum per head across the 4 lane
 //     groups (permlane swaps), lazily moved reference maximum, p = 2^(s - m);
-//   * P . V on v_mfma_f32_16x16x16 (f16 for the e4m3 cache: p rounded to f16,
+//   * P . V on v_mfma_f32_16x16x16 (f16 for the FP8 caches: p rounded to f16,
 //     V widened to f16 exactly; bf16 for the bf16 cache with p split into a
 //     bf16 high and low part, two products): lane (n, g) already holds P for
 //     head n and keys 4g..4g+3, the A operand.  V is written to a small
@@ -218,10 +218,11 @@ __device__ __forceinline__ void merge_rows(const float* o_in, const float* m_in,
 }
 
 
-// 8 e4m3 codes (two dwords) -> 8 bf16 (exact)
-__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
-  const bf16x2 a = e4m3x2_to_bf16<false>(w0), b = e4m3x2_to_bf16<true>(w0);
-  const bf16x2 c = e4m3x2_to_bf16<false>(w1), d = e4m3x2_to_bf16<true>(w1);
+// 8 FP8 codes (two dwords) -> 8 bf16 (exact for e4m3 and e5m2)
+template <int kFmt>
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  const bf16x2 a = fp8x2_to_bf16<kFmt, false>(w0), b = fp8x2_to_bf16<kFmt, true>(w0);
+  const bf16x2 c = fp8x2_to_bf16<kFmt, false>(w1), d = fp8x2_to_bf16<kFmt, true>(w1);
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
@@ -229,13 +230,14 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast
 
 // Waves per SIMD the register budget is sized for, without spills: four at
 // head_dim 64, three at 128, two at 256.
-template <int D, bool kFp8>
+template <int D, int kFmt>
 constexpr int decode_min_waves() {
   return D == 64 ? 4 : D == 128 ? 3 : 2;
 }
 
-template <int D, int G, bool kFp8, int NW, int PD>
-__global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFp8>())) void decode_split_kernel(DecodeParams p) {
+template <int D, int G, int kFmt, int NW, int PD>
+__global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFmt>())) void decode_split_kernel(DecodeParams p) {
+  constexpr bool kFp8 = kFmt != kFmtBf16;
   constexpr int ES = kFp8 ? 1 : 2;       // bytes per element
   constexpr int ROW = D * ES;            // bytes per cached row
   constexpr int HALF = kBlockSize * ROW; // K (or V) bytes of one page-head
@@ -264,7 +266,7 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFp8>())) void decode
   const int pg1 = min(pg0 + p.pages_per_split, page_hi);
 
   // ---- query operand: chunk q holds, for lane group g, head-dim elements
-  //      e4m3 cache: 64*(q/2) + 16*g + 8*(q%2) + i;  bf16 cache: 32*q + 8*g + i
+  //      FP8 cache: 64*(q/2) + 16*g + 8*(q%2) + i;  bf16 cache: 32*q + 8*g + i
   bf16x8 qop[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
@@ -322,11 +324,11 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFp8>())) void decode
       const int e0 = kFp8 ? 64 * hh + 16 * g : 32 * hh + 8 * g;   // first element of the piece
       uint4 kc, vc;
       if (p.new_bf16) {
-        kc = encode_chunk<true, kFp8>(p.k_new, src0 + e0, ks);
-        vc = encode_chunk<true, kFp8>(p.v_new, src0 + e0, vs);
+        kc = encode_chunk<true, kFmt>(p.k_new, src0 + e0, ks);
+        vc = encode_chunk<true, kFmt>(p.v_new, src0 + e0, vs);
       } else {
-        kc = encode_chunk<false, kFp8>(p.k_new, src0 + e0, ks);
-        vc = encode_chunk<false, kFp8>(p.v_new, src0 + e0, vs);
+        kc = encode_chunk<false, kFmt>(p.k_new, src0 + e0, ks);
+        vc = encode_chunk<false, kFmt>(p.v_new, src0 + e0, vs);
       }
       *reinterpret_cast<uint4*>(dst + 64 * hh) = kc;
       *reinterpret_cast<uint4*>(dst + HALF + 64 * hh) = vc;
@@ -353,7 +355,7 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFp8>())) void decode
       bf16x8 a;
       if constexpr (kFp8) {
         const uint4 w = pg.k[q / 2];
-        a = (q % 2 == 0) ? e4m3x8_to_bf16(w.x, w.y) : e4m3x8_to_bf16(w.z, w.w);
+        a = (q % 2 == 0) ? fp8x8_to_bf16<kFmt>(w.x, w.y) : fp8x8_to_bf16<kFmt>(w.z, w.w);
       } else {
         a = as_bf16x8(pg.k[q]);
       }
@@ -364,7 +366,7 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFp8>())) void decode
     // only the pages at the window start / sequence end hold invisible keys
     // (their V rows are zeroed as operands too: the rows past the sequence end
     // hold whatever the page held before, and 0 * NaN would be NaN)
-    uint32_t vmask_lo = ~0u, vmask_hi = ~0u;   // byte (e4m3) or half-word (bf16) masks
+    uint32_t vmask_lo = ~0u, vmask_hi = ~0u;   // byte (FP8) or half-word (bf16) masks
     if (page * kBlockSize < lo || page * kBlockSize + kBlockSize > L) {
       uint32_t bits = 0;
 #pragma unroll
@@ -426,8 +428,8 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFp8>())) void decode
           const i32x2 t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
               (lds_i32x2_ptr)(sv + (4 * g + (j & 3)) * RS + 16 * cb + 8 * (n & 1)));
           const uint32_t codes = (uint32_t)t[0] & vmask_lo;
-          const f16x2 v01 = e4m3x2_to_f16<false>(codes);
-          const f16x2 v23 = e4m3x2_to_f16<true>(codes);
+          const f16x2 v01 = fp8x2_to_f16<kFmt, false>(codes);
+          const f16x2 v23 = fp8x2_to_f16<kFmt, true>(codes);
           const f16x4 vb = {v01[0], v01[1], v23[0], v23[1]};
           o[hh * BPS + cb] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vb, o[hh * BPS + cb], 0, 0, 0);
         }
@@ -632,33 +634,43 @@ void decode_workspace_carve(void* ws, int batch, int num_q_heads, int head_dim, 
 #define FA8_DECODE_PIPE 2      // pages in flight per wave
 #endif
 
-template <int D, int G, bool kFp8>
+template <int D, int G, int kFmt>
 static void launch_shape(const DecodeParams& p, dim3 grid, hipStream_t stream) {
   constexpr int NW = kDecodeWaves;
-  hipLaunchKernelGGL((decode_split_kernel<D, G, kFp8, NW, FA8_DECODE_PIPE>), grid, dim3(64 * NW),
+  hipLaunchKernelGGL((decode_split_kernel<D, G, kFmt, NW, FA8_DECODE_PIPE>), grid, dim3(64 * NW),
                      0, stream, p);
 }
 
-template <int D, bool kFp8>
+template <int D, int kFmt>
 static hipError_t launch_decode_d(const DecodeParams& p, hipStream_t stream) {
   const int G = p.num_q_heads / p.num_kv_heads;
   const dim3 grid(p.num_splits, p.num_kv_heads, p.batch);
   switch (G) {
-    case 1: launch_shape<D, 1, kFp8>(p, grid, stream); break;
-    case 2: launch_shape<D, 2, kFp8>(p, grid, stream); break;
-    case 4: launch_shape<D, 4, kFp8>(p, grid, stream); break;
-    case 8: launch_shape<D, 8, kFp8>(p, grid, stream); break;
-    case 16: launch_shape<D, 16, kFp8>(p, grid, stream); break;
+    case 1: launch_shape<D, 1, kFmt>(p, grid, stream); break;
+    case 2: launch_shape<D, 2, kFmt>(p, grid, stream); break;
+    case 4: launch_shape<D, 4, kFmt>(p, grid, stream); break;
+    case 8: launch_shape<D, 8, kFmt>(p, grid, stream); break;
+    case 16: launch_shape<D, 16, kFmt>(p, grid, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeParams& p, bool fp8_cache, hipStream_t stream) {
+template <int kFmt>
+static hipError_t launch_decode_f(const DecodeParams& p, hipStream_t stream) {
   switch (p.head_dim) {
-    case 64: return fp8_cache ? launch_decode_d<64, true>(p, stream) : launch_decode_d<64, false>(p, stream);
-    case 128: return fp8_cache ? launch_decode_d<128, true>(p, stream) : launch_decode_d<128, false>(p, stream);
-    case 256: return fp8_cache ? launch_decode_d<256, true>(p, stream) : launch_decode_d<256, false>(p, stream);
+    case 64: return launch_decode_d<64, kFmt>(p, stream);
+    case 128: return launch_decode_d<128, kFmt>(p, stream);
+    case 256: return launch_decode_d<256, kFmt>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode(const DecodeParams& p, int fmt, hipStream_t stream) {
+  switch (fmt) {
+    case kFmtE4m3: return launch_decode_f<kFmtE4m3>(p, stream);
+    case kFmtE5m2: return launch_decode_f<kFmtE5m2>(p, stream);
+    case kFmtBf16: return launch_decode_f<kFmtBf16>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

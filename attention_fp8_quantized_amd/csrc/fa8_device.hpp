@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa8_internal.hpp"   // kFmt* cache formats
+
 namespace fa8 {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -44,6 +46,40 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y) {
   return code | sign;
 }
 
+// ---------------------------------------------------------------------------
+// e5m2 encoding (OCP E5M2: bias 15, 2 mantissa bits, max finite 57344), the
+// same rules as e4m3: round-to-nearest-even, saturation at +-57344 (also for
+// +-inf: the cache never holds an infinity), NaN -> 0x7F with the input's
+// sign, sign of zero kept.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e5m2_encode(float y) {
+  const uint32_t bits = __float_as_uint(y);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const uint32_t a = bits & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a > 0x7F800000u) {
+    code = 0x7Fu;                        // NaN
+  } else if (a >= 0x47600000u) {
+    code = 0x7Bu;                        // |y| >= 57344 (incl. inf): saturate
+  } else if (a < 0x38800000u) {
+    // |y| < 2^-14: subnormal codes m * 2^-16, m = rne(|y| * 2^16) in 0..4
+    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 65536.0f);
+  } else {
+    // normal: keep 2 of the 23 mantissa bits with ties-to-even, then rebias
+    // the exponent from 127 to 15; a mantissa carry moves into the exponent
+    const uint32_t r = a + 0xFFFFFu + ((a >> 21) & 1u);
+    code = (r >> 21) - (112u << 2);
+  }
+  return code | sign;
+}
+
+template <int kFmt>
+__device__ __forceinline__ uint32_t fp8_encode(float y) {
+  static_assert(kFmt == kFmtE4m3 || kFmt == kFmtE5m2, "FP8 format");
+  if constexpr (kFmt == kFmtE4m3) return e4m3_encode(y);
+  else return e5m2_encode(y);
+}
+
 // fp32 -> bf16 bits, round-to-nearest-even; NaN stays a (quiet) NaN.
 __device__ __forceinline__ uint32_t bf16_bits(float x) {
   const uint32_t u = __float_as_uint(x);
@@ -70,6 +106,31 @@ __device__ __forceinline__ bf16x2 e4m3x2_to_bf16(uint32_t w) {
 template <bool kHi>
 __device__ __forceinline__ f16x2 e4m3x2_to_f16(uint32_t w) {
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, kHi);
+}
+
+// Two e5m2 codes -> bf16 / f16 pairs (exact: e5m2 is the top byte of an
+// f16, and bf16 has more exponent and mantissa bits than e5m2).
+template <bool kHi>
+__device__ __forceinline__ bf16x2 e5m2x2_to_bf16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, kHi);
+}
+
+template <bool kHi>
+__device__ __forceinline__ f16x2 e5m2x2_to_f16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w, 1.0f, kHi);
+}
+
+// Format-generic forms of the two widenings above.
+template <int kFmt, bool kHi>
+__device__ __forceinline__ bf16x2 fp8x2_to_bf16(uint32_t w) {
+  if constexpr (kFmt == kFmtE5m2) return e5m2x2_to_bf16<kHi>(w);
+  else return e4m3x2_to_bf16<kHi>(w);
+}
+
+template <int kFmt, bool kHi>
+__device__ __forceinline__ f16x2 fp8x2_to_f16(uint32_t w) {
+  if constexpr (kFmt == kFmtE5m2) return e5m2x2_to_f16<kHi>(w);
+  else return e4m3x2_to_f16<kHi>(w);
 }
 
 // acc + a.x*b.x + a.y*b.y  (products of f16 are exact in fp32)
@@ -112,11 +173,13 @@ __device__ __forceinline__ float group_sum(float x) {
 }
 
 // One 16-byte chunk of a cached row from its input elements (fp32 or bf16):
-// 16 e4m3 codes of fl32(x / scale) (correctly rounded quotient: callers are
-// built without fast-math and with correctly rounded division), or 8 bf16
-// values (scale unused).  `elem` indexes the input in elements.
-template <bool kInBf16, bool kFp8Cache>
+// 16 FP8 codes (kFmt e4m3 or e5m2) of fl32(x / scale) (correctly rounded
+// quotient: callers are built without fast-math and with correctly rounded
+// division), or 8 bf16 values (kFmtBf16, scale unused).  `elem` indexes the
+// input in elements.
+template <bool kInBf16, int kFmt>
 __device__ __forceinline__ uint4 encode_chunk(const void* src, int64_t elem, float scale) {
+  constexpr bool kFp8Cache = kFmt != kFmtBf16;
   constexpr int N = kFp8Cache ? 16 : 8;
   float x[N];
   if constexpr (kInBf16) {
@@ -148,7 +211,7 @@ __device__ __forceinline__ uint4 encode_chunk(const void* src, int64_t elem, flo
     for (int w = 0; w < 4; ++w) {
       uint32_t word = 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) word |= e4m3_encode(x[w * 4 + j] / scale) << (8 * j);
+      for (int j = 0; j < 4; ++j) word |= fp8_encode<kFmt>(x[w * 4 + j] / scale) << (8 * j);
       packed[w] = word;
     }
   } else {

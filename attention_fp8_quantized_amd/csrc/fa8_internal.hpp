@@ -8,10 +8,15 @@
 
 namespace fa8 {
 
+// Element formats of the paged cache (template arguments of the kernels).
+constexpr int kFmtBf16 = 0;   // bf16 values, 2 bytes
+constexpr int kFmtE4m3 = 1;   // OCP E4M3 codes, 1 byte
+constexpr int kFmtE5m2 = 2;   // OCP E5M2 codes, 1 byte
+
 hipError_t launch_cache_write(const void* k, const void* v, bool in_bf16,
                               int64_t n_tokens, int num_kv_heads, int head_dim,
                               const int64_t* slot_mapping, const float* k_scale,
-                              const float* v_scale, void* cache, bool fp8_cache,
+                              const float* v_scale, void* cache, int fmt,
                               hipStream_t stream);
 
 // Per-KV-head absmax scales of k and v: three launches (zero, reduce,
@@ -69,12 +74,13 @@ size_t decode_workspace_bytes(int batch, int num_q_heads, int head_dim, int spli
 void decode_workspace_carve(void* ws, int batch, int num_q_heads, int head_dim, int splits,
                             DecodeParams& p);
 
-hipError_t launch_decode(const DecodeParams& p, bool fp8_cache, hipStream_t stream);
+// fmt: kFmtE4m3, kFmtE5m2 or kFmtBf16 (fa8_device.hpp)
+hipError_t launch_decode(const DecodeParams& p, int fmt, hipStream_t stream);
 
 struct PrefillParams {
   const uint16_t* q;          // bf16 [Tq][Hq][D]
   const int32_t* cu_q_lens;   // [B+1]
-  const uint8_t* cache;       // e4m3 [nb][Hkv][2][16][D]
+  const uint8_t* cache;       // FP8 codes [nb][Hkv][2][16][D]
   const int32_t* block_table; // [B][max_blocks]
   const int32_t* seq_lens;    // [B] (context incl. the chunk)
   const float* q_scale;       // [1]
@@ -83,6 +89,7 @@ struct PrefillParams {
   float* out;                 // [Tq][Hq][D]
   int batch, num_q_heads, num_kv_heads, head_dim, max_blocks, max_q_len;
   int window, accum_mode;
+  int fmt;                    // cache format: kFmtE4m3 or kFmtE5m2
   float sm_scale;
 };
 

@@ -7,20 +7,24 @@
 // Quantization Fusion": the query is quantised with a per-tensor scale right
 // before attention -- here in the kernel's prologue.
 //
-// Work decomposition: one workgroup of 4 waves per (64 query rows, query
+// The cache holds e4m3 or e5m2 codes ([GPUSTACK] "KV キャッシュの量子化"
+// names both FP8 cache formats); the query and P are always e4m3.
+//
+// Work decomposition: one workgroup of 8 waves per (128 query rows, query
 // head, sequence); each wave owns 16 query rows.  Keys are visited in tiles
 // of 128 at absolute, 128-aligned positions, in ascending order (this order
 // and width are part of the numeric contract, see fa8_prefill_kv_tile).
 //
 // Per KV tile:
-//   * the tile's K and V rows (8 pages, e4m3) are copied into LDS with
-//     16-byte loads, whole rows per load instruction; the block ids of the
-//     next tile are fetched during the current one;
+//   * the tile's K and V rows (8 pages of FP8 codes) are copied straight
+//     into LDS (global_load_lds, 16 bytes per lane) with the next tile's
+//     copies in flight during the current tile (two buffers); the block ids
+//     two tiles ahead are fetched meanwhile;
 //   * S^T = K . Q^T on v_mfma_f32_16x16x32_bf16: the A operand is 8 K codes
 //     of one key row per lane, widened to bf16 after the LDS read (exact:
-//     bf16 holds every e4m3 value), the B operand the e4m3-quantised query
+//     bf16 holds every e4m3 and e5m2 value), the B operand the e4m3 query
 //     (decoded to bf16, exact; held in registers for the whole kernel).  The
-//     products are exactly the e4m3 x e4m3 products; the bf16 MFMA sums
+//     products are exactly the FP8 x FP8 products; the bf16 MFMA sums
 //     them in fp32.  (The FP8 MFMA of this chip sums its 128 products with
 //     about 13 bits below the largest one; the scores decide how each p
 //     rounds to e4m3, so they are formed with fp32 sums.)  The result leaves
@@ -54,9 +58,12 @@ constexpr float kNegInfP = -__builtin_huge_valf();
 
 int prefill_kv_tile(int) { return kTileN; }
 
-__device__ __forceinline__ f32x4 mfma_fp8(i32x8 a, i32x8 b, f32x4 c) {
-  // e4m3 x e4m3 (cbsz = blgp = 0), unit block scales (E8M0 127 = 2^0)
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+// P~ (e4m3, A operand: cbsz = 0) times V~ (the cache's FP8 format, B
+// operand: blgp = 0 for e4m3, 1 for e5m2), unit block scales (E8M0 127 = 2^0)
+template <int kFmt>
+__device__ __forceinline__ f32x4 mfma_pv(i32x8 a, i32x8 b, f32x4 c) {
+  constexpr int kBlgp = kFmt == kFmtE5m2 ? 1 : 0;
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, kBlgp, 0, 127, 0, 127);
 }
 
 typedef int i32x2 __attribute__((ext_vector_type(2)));
@@ -100,7 +107,7 @@ __device__ __forceinline__ int swz(int r) {
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
-template <int D>
+template <int D, int kFmt>
 __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
   constexpr int KQ = D / 32;               // 32-wide chunks of the head dim (bf16 MFMA K)
   constexpr int DB = D / 16;               // 16-wide output column blocks
@@ -263,8 +270,8 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
 #pragma unroll
       for (int kq = 0; kq < KQ; ++kq) {
         const uint2 a = *reinterpret_cast<const uint2*>(krow + (((2 * kq + (g >> 1)) ^ ksw) * 16));
-        const bf16x2 a0 = e4m3x2_to_bf16<false>(a.x), a1 = e4m3x2_to_bf16<true>(a.x);
-        const bf16x2 a2 = e4m3x2_to_bf16<false>(a.y), a3 = e4m3x2_to_bf16<true>(a.y);
+        const bf16x2 a0 = fp8x2_to_bf16<kFmt, false>(a.x), a1 = fp8x2_to_bf16<kFmt, true>(a.x);
+        const bf16x2 a2 = fp8x2_to_bf16<kFmt, false>(a.y), a3 = fp8x2_to_bf16<kFmt, true>(a.y);
         const bf16x8 av = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
         s[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[kq], s[mb], 0, 0, 0);
       }
@@ -357,7 +364,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
         const i32x8 vb = vb_next;
         if (db + 1 < DB) vb_next = load_vb(db + 1);
         // level 1: this tile's P.V into a zeroed accumulator; level 2: fp32 flush
-        const f32x4 acc = mfma_fp8(pa, vb, f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 acc = mfma_pv<kFmt>(pa, vb, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[db][i] = alpha_o[i] * o[db][i] + acc[i];
         __builtin_amdgcn_sched_barrier(0);
@@ -371,7 +378,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
         f32x4 c;
 #pragma unroll
         for (int i = 0; i < 4; ++i) c[i] = alpha_o[i] * o[db][i];
-        o[db] = mfma_fp8(pa, vb, c);
+        o[db] = mfma_pv<kFmt>(pa, vb, c);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -401,21 +408,26 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
   }
 }
 
-template <int D>
-static void launch_prefill_d(const PrefillParams& p, dim3 grid, dim3 block, hipStream_t stream) {
-  hipLaunchKernelGGL(prefill_kernel<D>, grid, block, 0, stream, p);
+template <int kFmt>
+static hipError_t launch_prefill_f(const PrefillParams& p, dim3 grid, dim3 block,
+                                   hipStream_t stream) {
+  switch (p.head_dim) {
+    case 64: hipLaunchKernelGGL((prefill_kernel<64, kFmt>), grid, block, 0, stream, p); break;
+    case 128: hipLaunchKernelGGL((prefill_kernel<128, kFmt>), grid, block, 0, stream, p); break;
+    case 256: hipLaunchKernelGGL((prefill_kernel<256, kFmt>), grid, block, 0, stream, p); break;
+    default: return hipErrorNotSupported;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   dim3 grid((p.max_q_len + kBlockM - 1) / kBlockM, p.num_q_heads, p.batch);
   dim3 block(64 * kWaves);
-  switch (p.head_dim) {
-    case 64: launch_prefill_d<64>(p, grid, block, stream); break;
-    case 128: launch_prefill_d<128>(p, grid, block, stream); break;
-    case 256: launch_prefill_d<256>(p, grid, block, stream); break;
+  switch (p.fmt) {
+    case kFmtE4m3: return launch_prefill_f<kFmtE4m3>(p, grid, block, stream);
+    case kFmtE5m2: return launch_prefill_f<kFmtE5m2>(p, grid, block, stream);
     default: return hipErrorNotSupported;
   }
-  return hipGetLastError();
 }
 
 }  // namespace fa8

@@ -22,7 +22,8 @@
  *       cache[num_blocks][num_kv_heads][2][16][head_dim]
  *   index 2 is 0 = K, 1 = V; 16 tokens per block (page).  A token with slot
  *   id t lives in block t / 16, row t % 16.  Element type: one byte per
- *   element (e4m3 code) for FA8_E4M3, two (bf16 bits) for FA8_BF16.  The
+ *   element for the FP8 caches (an e4m3 code for FA8_E4M3, an e5m2 code for
+ *   FA8_E5M2), two (bf16 bits) for FA8_BF16.  The
  *   K rows and the V rows of one (block, head) are each 16*head_dim elements
  *   of contiguous memory.
  * - Scales: k_scale[num_kv_heads], v_scale[num_kv_heads] fp32 in device
@@ -54,7 +55,14 @@ typedef enum {
   FA8_EHIP = 3
 } fa8_status;
 
-typedef enum { FA8_F32 = 0, FA8_BF16 = 1, FA8_E4M3 = 2 } fa8_dtype;
+/*
+ * FA8_E5M2 is the OCP OFP8 E5M2 encoding (bias 15, max finite 57344,
+ * S.11111.00 = inf, other exponent-31 codes NaN), the second FP8 cache format
+ * [GPUSTACK] "KV キャッシュの量子化" names.  Both FP8 caches follow one
+ * contract: round-to-nearest-even, saturation at the largest finite value
+ * (so an e5m2 cache never holds an infinity), NaN -> 0x7F|sign.
+ */
+typedef enum { FA8_F32 = 0, FA8_BF16 = 1, FA8_E4M3 = 2, FA8_E5M2 = 3 } fa8_dtype;
 
 #define FA8_BLOCK_SIZE 16
 
@@ -68,10 +76,12 @@ typedef enum { FA8_F32 = 0, FA8_BF16 = 1, FA8_E4M3 = 2 } fa8_dtype;
  *                 FA8_BF16, row-major, contiguous.
  *   slot_mapping  int64 [n_tokens]; a negative slot skips the row (padding).
  *                 Slots must be < num_blocks*16 and pairwise distinct.
- *   cache         see the layout above; cache_dtype FA8_E4M3 or FA8_BF16.
+ *   cache         see the layout above; cache_dtype FA8_E4M3, FA8_E5M2 or
+ *                 FA8_BF16.
  * FA8_E4M3: code = e4m3(fl32(x / scale[h])) with the fp32 quotient
  *   correctly rounded, then round-to-nearest-even, saturation at +-448
  *   (also for +-inf), NaN -> 0x7F|sign, sign of zero kept.
+ * FA8_E5M2: the same with e5m2 codes, saturation at +-57344.
  * FA8_BF16: the bf16 rounding (nearest-even) of x; scales are not read and
  *   may be NULL (layers kept in BF16, [BLOG] "Skipping layers").
  * n_tokens == 0 is a no-op.
@@ -94,10 +104,11 @@ fa8_status fa8_cache_write(const void* k, const void* v, int32_t in_dtype,
  *   k, v          [n_tokens][num_kv_heads][head_dim], in_dtype FA8_F32 or
  *                 FA8_BF16, row-major, contiguous (the same rows
  *                 fa8_cache_write takes).
- *   cache_dtype   FA8_E4M3: the largest finite code value, 448, is the
- *                 target of each head's largest magnitude.
+ *   cache_dtype   the FP8 format the scales are for: each head's largest
+ *                 magnitude maps onto the format's largest finite value,
+ *                 F = 448 for FA8_E4M3, 57344 for FA8_E5M2.
  *   k_scale, v_scale  fp32 [num_kv_heads], written:
- *       scale[h] = max(fl32(absmax_h / 448), 2^-126)
+ *       scale[h] = max(fl32(absmax_h / F), 2^-126)
  *   with absmax_h the largest |x| over all finite entries of head h (NaN
  *   and +-inf are skipped; no rows or all zeros give the floor 2^-126) and
  *   the fp32 quotient correctly rounded.  The result is exact: it does not
@@ -142,7 +153,7 @@ size_t fa8_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
  *   seq_lens     int32 [batch]; the query is token seq_lens[b]-1, whose K/V
  *                must already be in the cache.  0 gives a zero output row.
  *   max_seq_len  host upper bound of seq_lens (sizes the grid only).
- *   k_scale/v_scale  per-KV-head scales (read for FA8_E4M3 only).
+ *   k_scale/v_scale  per-KV-head scales (read for the FP8 caches only).
  *   sm_scale     softmax scale (usually 1/sqrt(head_dim)).
  *   window       > 0: attend to the last `window` keys (the query's own
  *                token included); <= 0: the whole context.
@@ -156,7 +167,7 @@ size_t fa8_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
  *                without clearing.  Calls that share a workspace must be
  *                ordered on one stream.
  * Supported: head_dim in {64, 128, 256}; num_q_heads / num_kv_heads in
- * {1, 2, 4, 8, 16}; cache_dtype FA8_E4M3 or FA8_BF16.
+ * {1, 2, 4, 8, 16}; cache_dtype FA8_E4M3, FA8_E5M2 or FA8_BF16.
  */
 fa8_status fa8_decode_attention(const void* q, int32_t batch,
                                 int32_t num_q_heads, const void* cache,
@@ -222,7 +233,10 @@ int32_t fa8_prefill_kv_tile(int32_t head_dim);
  *   seq_lens   int32 [batch]: context length INCLUDING this chunk; the
  *              chunk's queries sit at positions seq_len - q_len .. seq_len-1
  *              and their K/V must already be in the cache.
- *   q_scale    fp32 [1] device: q8 = e4m3(fl32(q / q_scale)).
+ *   q_scale    fp32 [1] device: q8 = e4m3(fl32(q / q_scale)) (the query is
+ *              e4m3 whatever the cache's FP8 format).
+ *   cache_dtype  FA8_E4M3 or FA8_E5M2: the format of K and V codes.  P is
+ *              always e4m3; the P*V matrix product takes e5m2 V directly.
  *   window     as in decode, counted from each query's own position.
  *   accum_mode 1 = two-level (MFMA sums each KV tile into a zeroed fp32
  *              register tile, then O = alpha*O + tile in fp32; default);
@@ -230,11 +244,12 @@ int32_t fa8_prefill_kv_tile(int32_t head_dim);
  *   out        fp32 [total_q][num_q_heads][head_dim].
  * Per row and KV tile t (width fa8_prefill_kv_tile): running max m_t,
  * p = exp(s - m_t) in fp32, P*V uses e4m3(p), the denominator the fp32 p.
- * Supported: head_dim in {64, 128, 256}; cache_dtype FA8_E4M3 only.
+ * Supported: head_dim in {64, 128, 256}; cache_dtype FA8_E4M3 or FA8_E5M2.
  */
 fa8_status fa8_prefill_attention(const void* q, const int32_t* cu_q_lens,
                                  int32_t batch, int32_t num_q_heads,
                                  int32_t max_q_len, const void* cache,
+                                 int32_t cache_dtype,
                                  int64_t num_blocks, int32_t num_kv_heads,
                                  int32_t head_dim, const int32_t* block_table,
                                  int32_t max_blocks_per_seq,

@@ -79,7 +79,8 @@ class DecodeCase:
             k = W.with_outliers(k, W.rng(seed, 0, W.OUTLIERS))
             v = W.with_outliers(v, W.rng(seed, 1, W.OUTLIERS))
         if scales == "absmax" and N:
-            self.ks, self.vs = W.absmax_scales(k), W.absmax_scales(v)
+            fm = W.FMT_MAX.get(cache_dtype, W.E4M3_MAX)
+            self.ks, self.vs = W.absmax_scales(k, fm), W.absmax_scales(v, fm)
         else:
             self.ks = self.vs = np.ones(Hkv, dtype=np.float32)
         self.slots = W.all_slots(self.bt, self.lens)
@@ -153,11 +154,12 @@ class DecodeCase:
 
 
 class PrefillCase:
-    """Chunked prefill over a paged e4m3 cache: sequence b has context
-    lens[b] whose last qlens[b] tokens are the queries (packed by cu)."""
+    """Chunked prefill over a paged FP8 cache (e4m3 or e5m2 codes): sequence
+    b has context lens[b] whose last qlens[b] tokens are the queries (packed
+    by cu)."""
 
     def __init__(self, qlens, lens, Hq, Hkv, D, seed=0, window=0, q_zero=False,
-                 q_scale="absmax", fill=0):
+                 q_scale="absmax", fill=0, cache_dtype="e4m3"):
         import torch
         import attention_fp8_quantized_amd as fa
         self.qlens = np.asarray(qlens, dtype=np.int32)
@@ -170,7 +172,9 @@ class PrefillCase:
         N = int(self.lens.sum())
         k = W.normal(W.rng(seed, 0, W.K), (N, Hkv, D))
         v = W.normal(W.rng(seed, 0, W.V), (N, Hkv, D))
-        self.ks, self.vs = W.absmax_scales(k), W.absmax_scales(v)
+        self.cd = cache_dtype
+        fm = W.FMT_MAX[cache_dtype]
+        self.ks, self.vs = W.absmax_scales(k, fm), W.absmax_scales(v, fm)
         self.slots = W.all_slots(self.bt, self.lens)
         need = W.blocks_needed(self.lens)
         for b, nb in enumerate(need):
@@ -185,7 +189,7 @@ class PrefillCase:
         else:
             self.qs = np.array([q_scale], np.float32)
         self.k, self.v = k, v
-        self.cache = fa.new_cache(self.nblocks, Hkv, D, "e4m3")
+        self.cache = fa.new_cache(self.nblocks, Hkv, D, cache_dtype)
         self.cache.view(torch.uint8).fill_(fill)
         fa.cache_write(dev(k), dev(v), dev(self.slots), dev(self.ks), dev(self.vs), self.cache)
         self.q_dev = qb.cuda()
@@ -206,9 +210,9 @@ class PrefillCase:
 
     def oracle_cache(self):
         if self._oracle_cache is None:
-            c = OQ.new_cache(self.nblocks, self.Hkv, self.D, "e4m3")
+            c = OQ.new_cache(self.nblocks, self.Hkv, self.D, self.cd)
             self._oracle_cache = OQ.cache_write(c, self.k, self.v, self.slots, self.ks, self.vs,
-                                                "e4m3")
+                                                self.cd)
         return self._oracle_cache
 
     # float32 score and exp2 error of the kernel, relative, with a 4x margin
@@ -222,6 +226,6 @@ class PrefillCase:
         args = (self.q, self.cu, self.oracle_cache(), self.bt, self.lens, self.qs[0], self.ks,
                 self.vs, self.sm, self.window)
         if exact:
-            return OA.prefill_exact(*args, rows=rows)
+            return OA.prefill_exact(*args, rows=rows, cache_dtype=self.cd)
         return OA.prefill_mirror(*args, kv_tile=fa.prefill_kv_tile(self.D), rows=rows,
-                                 flip_tol=self.FLIP_TOL)
+                                 flip_tol=self.FLIP_TOL, cache_dtype=self.cd)

@@ -121,6 +121,8 @@ def test_decode_rejects_bad_arguments(lib):
     assert _decode(lib, Hq=6, Hkv=2) == EUNSUPPORTED         # G = 3
     assert _decode(lib, D=96) == EUNSUPPORTED
     assert _decode(lib, cd=0) == EINVAL
+    assert _decode(lib, cd=4) == EINVAL
+    assert _decode(lib, cd=3, ks=None) == EINVAL             # e5m2 needs scales too
     assert _decode(lib, maxlen=65) == EINVAL                 # 4 blocks hold 64 tokens
     assert _decode(lib, wsb=100) == EINVAL
     assert b"workspace" in lib.fa8_last_error()
@@ -158,18 +160,21 @@ def test_prefill_rejects_bad_arguments(lib):
     fake = _p(0x1000)
 
     def call(**over):
-        a = dict(q=fake, cu=fake, B=1, Hq=8, mq=16, cache=fake, nb=4, Hkv=2, D=64, bt=fake,
-                 mb=4, lens=fake, qs=fake, ks=fake, vs=fake, sm=0.125, window=0, acc=1,
-                 out=fake)
+        a = dict(q=fake, cu=fake, B=1, Hq=8, mq=16, cache=fake, cd=2, nb=4, Hkv=2, D=64,
+                 bt=fake, mb=4, lens=fake, qs=fake, ks=fake, vs=fake, sm=0.125, window=0,
+                 acc=1, out=fake)
         a.update(over)
         return lib.fa8_prefill_attention(a["q"], a["cu"], a["B"], a["Hq"], a["mq"], a["cache"],
-                                         a["nb"], a["Hkv"], a["D"], a["bt"], a["mb"], a["lens"],
+                                         a["cd"], a["nb"], a["Hkv"], a["D"], a["bt"], a["mb"],
+                                         a["lens"],
                                          a["qs"], a["ks"], a["vs"], a["sm"], a["window"],
                                          a["acc"], a["out"], None)
 
     assert call(Hq=7) == EINVAL
     assert call(D=80) == EUNSUPPORTED
     assert call(acc=2) == EINVAL
+    assert call(cd=1) == EINVAL                  # prefill needs an FP8 cache
+    assert call(cd=4) == EINVAL
     assert call(qs=None) == EINVAL
     assert call(B=0) == 0
 
@@ -185,6 +190,7 @@ def test_absmax_scales_rejects_bad_arguments(lib):
 
     assert call(idt=2) == EINVAL                 # e4m3 is not an input type
     assert call(cd=1) == EINVAL                  # a bf16 cache takes no scales
+    assert call(cd=4) == EINVAL
     assert call(H=0) == EINVAL
     assert call(H=4097) == EINVAL
     assert call(D=96) == EUNSUPPORTED

@@ -1,7 +1,7 @@
 """GPU cache write vs the oracle: bit-exact cache bytes.
 
-e4m3 cache: code = e4m3(fl32(x / scale[h])) with round-to-nearest-even and
-saturation; bf16 cache: bf16 rounding of x.  Checked exhaustively over every
+e4m3 / e5m2 cache: code = fp8(fl32(x / scale[h])) with round-to-nearest-even
+and saturation; bf16 cache: bf16 rounding of x.  Checked exhaustively over every
 bf16 bit pattern at three scales, on random fp32 at several magnitudes, on an
 edge set (ties, saturation, inf, NaN, fp32 subnormals, signed zeros), through
 both input dtypes, and with a sentinel-filled cache to prove that only the
@@ -45,7 +45,7 @@ def _gpu_write(k, v, slots, ks, vs, nblocks, Hkv, D, cd, in_bf16=False, fill=Non
     out = cache.cpu()
     if cd == "bf16":
         return out.view(torch.int16).numpy().view(np.uint16)
-    return out.numpy()
+    return out.view(torch.uint8).numpy()
 
 
 def _oracle_write(k, v, slots, ks, vs, nblocks, Hkv, D, cd, fill=None):
@@ -57,8 +57,9 @@ def _all_bf16_as_f32():
     return (np.arange(65536, dtype=np.uint32) << 16).view(np.float32)
 
 
+@pytest.mark.parametrize("cd", ["e4m3", "e5m2"])
 @pytest.mark.parametrize("scale", [1.0, 0.0123, 2.0 ** -5])
-def test_exhaustive_bf16_patterns(scale):
+def test_exhaustive_bf16_patterns(scale, cd):
     Hkv, D = 2, 128
     x = _all_bf16_as_f32().reshape(-1, Hkv, D)             # 256 tokens
     v = -x[::-1].copy()
@@ -67,12 +68,12 @@ def test_exhaustive_bf16_patterns(scale):
     nblocks = (N + 32 + 15) // 16
     ks = np.full(Hkv, scale, np.float32)
     vs = np.array([scale, scale * 3], np.float32)
-    log(f"cache_write exhaustive bf16 patterns scale={scale}")
-    want = _oracle_write(x, v, slots, ks, vs, nblocks, Hkv, D, "e4m3", fill=0xA5)
-    got = _gpu_write(x, v, slots, ks, vs, nblocks, Hkv, D, "e4m3", fill=0xA5)
+    log(f"cache_write exhaustive bf16 patterns scale={scale} cache={cd}")
+    want = _oracle_write(x, v, slots, ks, vs, nblocks, Hkv, D, cd, fill=0xA5)
+    got = _gpu_write(x, v, slots, ks, vs, nblocks, Hkv, D, cd, fill=0xA5)
     assert np.array_equal(got, want)
     # same values arriving as bf16 tensors (exact: they are bf16 patterns)
-    got_b = _gpu_write(x, v, slots, ks, vs, nblocks, Hkv, D, "e4m3", in_bf16=True, fill=0xA5)
+    got_b = _gpu_write(x, v, slots, ks, vs, nblocks, Hkv, D, cd, in_bf16=True, fill=0xA5)
     assert np.array_equal(got_b, want)
 
 
@@ -82,12 +83,17 @@ def _edge_values():
     vals = [448, -448, 464, -464, 480, -480, ulp448, -ulp448, 2 ** -10, -2 ** -10,
             3 * 2 ** -11, 2 ** -6, np.nextafter(f(2 ** -6), f(0)), np.nextafter(f(2 ** -6), f(1)),
             1e-45, -1e-45, 1e-40, 0.0, -0.0, np.inf, -np.inf, np.nan, -np.nan, 1.0625, 1.1875,
-            3e38, -3e38, 432.0, 424.0]
+            3e38, -3e38, 432.0, 424.0,
+            # e5m2: saturation, ties, subnormal and smallest-normal edges
+            57344, -57344, 61440, -61440, 57345, np.nextafter(f(61440), f(0)), 1.125, 1.375,
+            1.875, 53248.0, 2 ** -17, 3 * 2 ** -17, 7 * 2 ** -17, 2 ** -14,
+            np.nextafter(f(2 ** -14), f(0))]
     return np.array(vals, dtype=np.float32)
 
 
+@pytest.mark.parametrize("cd", ["e4m3", "e5m2"])
 @pytest.mark.parametrize("D", [64, 128, 256])
-def test_random_and_edges(D):
+def test_random_and_edges(D, cd):
     g = np.random.default_rng(D)
     Hkv = 4
     N = 300
@@ -101,9 +107,9 @@ def test_random_and_edges(D):
     vs = g.uniform(0.001, 3.0, Hkv).astype(np.float32)
     slots = g.permutation(N * 2)[:N]
     nb = (N * 2 + 15) // 16
-    log(f"cache_write random+edges D={D}")
-    want = _oracle_write(k, v, slots, ks, vs, nb, Hkv, D, "e4m3", fill=0xA5)
-    got = _gpu_write(k, v, slots, ks, vs, nb, Hkv, D, "e4m3", fill=0xA5)
+    log(f"cache_write random+edges D={D} cache={cd}")
+    want = _oracle_write(k, v, slots, ks, vs, nb, Hkv, D, cd, fill=0xA5)
+    got = _gpu_write(k, v, slots, ks, vs, nb, Hkv, D, cd, fill=0xA5)
     assert np.array_equal(got, want)
 
 
@@ -145,8 +151,9 @@ def test_bf16_cache(in_bf16):
     assert np.array_equal(got[~nan_w], want[~nan_w])
 
 
+@pytest.mark.parametrize("cd", ["e4m3", "e5m2"])
 @pytest.mark.parametrize("N", [1, 8])
-def test_decode_step_sized_write(N):
+def test_decode_step_sized_write(N, cd):
     # one new token per sequence, Llama-shaped heads, per-head absmax scales
     Hkv, D = 8, 128
     g = W.rng(2, 0, W.K)
@@ -156,7 +163,7 @@ def test_decode_step_sized_write(N):
     vs = np.random.default_rng(6).uniform(0.002, 0.05, Hkv).astype(np.float32)
     slots = np.arange(N, dtype=np.int64) * 16 + 5
     nb = N
-    log(f"cache_write decode-step N={N}")
-    want = _oracle_write(k, v, slots, ks, vs, nb, Hkv, D, "e4m3", fill=0xA5)
-    got = _gpu_write(k, v, slots, ks, vs, nb, Hkv, D, "e4m3", fill=0xA5)
+    log(f"cache_write decode-step N={N} cache={cd}")
+    want = _oracle_write(k, v, slots, ks, vs, nb, Hkv, D, cd, fill=0xA5)
+    got = _gpu_write(k, v, slots, ks, vs, nb, Hkv, D, cd, fill=0xA5)
     assert np.array_equal(got, want)

@@ -30,10 +30,11 @@ def test_single_layer_hd64_ctx512_unit_scales():
     _check(c, "hd64 ctx512 unit scales")
 
 
-@pytest.mark.parametrize("cd", ["e4m3", "bf16"])
+@pytest.mark.parametrize("cd", ["e4m3", "e5m2", "bf16"])
 @pytest.mark.parametrize("ctx", [1024, 8192, 32768, 131072])
 def test_llama_shaped_layer(ctx, cd):
-    # 32 q / 8 KV heads, head_dim 128, outlier channels x20, absmax/448 scales
+    # 32 q / 8 KV heads, head_dim 128, outlier channels x20, per-head absmax
+    # scales (absmax/448 for e4m3, absmax/57344 for e5m2)
     heads = None if ctx <= 32768 else [0, 5]
     c = DecodeCase(1, 32, 8, 128, [ctx], cd, seed=2, outliers=True, oracle_heads=heads)
     _check(c, f"llama-shaped ctx={ctx} {cd}")
@@ -41,7 +42,7 @@ def test_llama_shaped_layer(ctx, cd):
 
 @pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
-@pytest.mark.parametrize("cd", ["e4m3", "bf16"])
+@pytest.mark.parametrize("cd", ["e4m3", "e5m2", "bf16"])
 def test_gqa_head_dims_ragged_batch(D, G, cd):
     Hkv = 2
     lens = [300, 0, 1, 17, 1000]
@@ -51,18 +52,18 @@ def test_gqa_head_dims_ragged_batch(D, G, cd):
 
 
 @pytest.mark.parametrize("window", [1, 16, 100, 128, 513])
-@pytest.mark.parametrize("cd", ["e4m3", "bf16"])
+@pytest.mark.parametrize("cd", ["e4m3", "e5m2", "bf16"])
 def test_sliding_window(window, cd):
     lens = [1000, 37, 128, 129]
     c = DecodeCase(len(lens), 16, 2, 64, lens, cd, seed=20 + window, window=window)
     _check(c, f"window={window} {cd}")
 
 
-@pytest.mark.parametrize("cd", ["e4m3", "bf16"])
+@pytest.mark.parametrize("cd", ["e4m3", "e5m2", "bf16"])
 def test_split_count_invariance(cd):
     # Splits only regroup the same sums, but each probability is rounded
     # relative to its split's running maximum, so the rounding pattern depends
-    # on how tokens are grouped: the e4m3 path rounds p to f16 (relative
+    # on how tokens are grouped: the FP8 paths round p to f16 (relative
     # 2^-11, ~1e-4 on the output), the bf16 path keeps p as a bf16 high + low
     # pair (relative 2^-18 per p, so two layouts differ by at most ~2^-17).
     c = DecodeCase(2, 32, 8, 128, [5000, 3333], cd, seed=30)
@@ -78,7 +79,7 @@ def test_split_count_invariance(cd):
         assert rl < tol, (s, rl)
 
 
-@pytest.mark.parametrize("cd", ["e4m3", "bf16"])
+@pytest.mark.parametrize("cd", ["e4m3", "e5m2", "bf16"])
 @pytest.mark.parametrize("window", [0, 100])
 def test_stale_nan_rows_past_sequence_end(cd, window):
     # pages are pre-filled with NaN codes; the rows past each sequence end
@@ -89,7 +90,7 @@ def test_stale_nan_rows_past_sequence_end(cd, window):
     assert np.all(np.isfinite(got))
 
 
-@pytest.mark.parametrize("cd", ["e4m3", "bf16"])
+@pytest.mark.parametrize("cd", ["e4m3", "e5m2", "bf16"])
 @pytest.mark.parametrize("in_dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("window", [0, 100])
 def test_fused_append_equals_write_then_decode(cd, in_dtype, window):

@@ -23,31 +23,35 @@ def _sample_rows(T, n, seed):
     return np.unique(np.concatenate([rest, tail])).astype(np.int64)
 
 
+@pytest.mark.parametrize("cd", ["e4m3", "e5m2"])
 @pytest.mark.parametrize("D", [64, 128, 256])
-def test_single_chunk_all_rows(D):
-    c = PrefillCase([200], [200], 4, 2, D, seed=D)
-    log(f"prefill D={D} T=200")
+def test_single_chunk_all_rows(D, cd):
+    c = PrefillCase([200], [200], 4, 2, D, seed=D, cache_dtype=cd)
+    log(f"prefill D={D} T=200 cache={cd}")
     got = c.run_gpu()
     ref, slack = c.oracle()
-    assert_gate(got, ref, f"D={D} T=200 mirror", slack=slack)
+    assert_gate(got, ref, f"D={D} T=200 {cd} mirror", slack=slack)
     ma, rl = metrics(got, c.oracle(exact=True))
     log(f"  vs unquantised-P reference: max_abs={ma:.3e} rel_l2={rl:.3e}")
 
 
+@pytest.mark.parametrize("cd", ["e4m3", "e5m2"])
 @pytest.mark.parametrize("window", [0, 100])
-def test_chunked_ragged_batch_gqa(window):
+def test_chunked_ragged_batch_gqa(window, cd):
     # three sequences: fresh (P=0), continued (P=300), short tail chunk
-    c = PrefillCase([130, 100, 17], [130, 400, 260], 8, 2, 128, seed=7, window=window)
-    log(f"prefill ragged window={window}")
+    c = PrefillCase([130, 100, 17], [130, 400, 260], 8, 2, 128, seed=7, window=window,
+                    cache_dtype=cd)
+    log(f"prefill ragged window={window} cache={cd}")
     ref, slack = c.oracle()
-    assert_gate(c.run_gpu(), ref, f"ragged batch window={window}", slack=slack)
+    assert_gate(c.run_gpu(), ref, f"ragged batch window={window} {cd}", slack=slack)
 
 
-def test_stale_nan_rows_past_sequence_end():
-    # pages are pre-filled with NaN codes; the rows past each sequence end
-    # keep them and must not reach the output
-    c = PrefillCase([130, 75], [130, 333], 4, 2, 128, seed=8, fill=0xFF)
-    log("prefill stale NaN rows")
+@pytest.mark.parametrize("cd", ["e4m3", "e5m2"])
+def test_stale_nan_rows_past_sequence_end(cd):
+    # pages are pre-filled with NaN codes (0xFF in both FP8 formats); the rows
+    # past each sequence end keep them and must not reach the output
+    c = PrefillCase([130, 75], [130, 333], 4, 2, 128, seed=8, fill=0xFF, cache_dtype=cd)
+    log(f"prefill stale NaN rows cache={cd}")
     got = c.run_gpu()
     assert np.all(np.isfinite(got))
     ref, slack = c.oracle()
@@ -86,6 +90,17 @@ def test_hd256_long_chunk_sampled(T):
     got = c.run_gpu()
     ref, slack = c.oracle(rows=rows)
     assert_gate(got[rows], ref, f"hd256 T={T} sampled", slack=slack)
+
+
+def test_e5m2_hd256_32k_sampled():
+    # the e5m2 cache at the large-head shape and the longest single chunk
+    T = 32768
+    c = PrefillCase([T], [T], 8, 1, 256, seed=14, cache_dtype="e5m2")
+    rows = _sample_rows(T, 48, seed=7)
+    log(f"prefill e5m2 hd256 T={T} (sampled {len(rows)} rows)")
+    got = c.run_gpu()
+    ref, slack = c.oracle(rows=rows)
+    assert_gate(got[rows], ref, f"e5m2 hd256 T={T} sampled", slack=slack)
 
 
 def test_last_chunk_of_128k_fill():

@@ -69,6 +69,21 @@ def test_non_finite_zero_heads_and_planted_maxima(in_bf16):
     assert gk[1] == np.float32(2.0 ** -126) and gv[3] == np.float32(2.0 ** -126)
 
 
+@pytest.mark.parametrize("in_bf16", [False, True])
+def test_e5m2_scales(in_bf16):
+    import torch
+    import attention_fp8_quantized_amd as fa
+    k, v = _inputs(6, (2000, 8, 128), in_bf16)
+    dt = torch.bfloat16 if in_bf16 else torch.float32
+    log(f"[absmax] e5m2 bf16={in_bf16}")
+    ks, vs = fa.absmax_scales(dev(k, dt), dev(v, dt), cache_dtype="e5m2")
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ks.cpu().numpy().view(np.uint32),
+                                  OQ.absmax_scales(k, OQ.E5M2_MAX).view(np.uint32))
+    np.testing.assert_array_equal(vs.cpu().numpy().view(np.uint32),
+                                  OQ.absmax_scales(v, OQ.E5M2_MAX).view(np.uint32))
+
+
 def test_empty_input_writes_the_floor():
     import torch
     import attention_fp8_quantized_amd as fa

@@ -23,6 +23,8 @@ import numpy as np
 
 BLOCK_SIZE = 16
 E4M3_MAX = 448.0
+E5M2_MAX = 57344.0
+FMT_MAX = {"e4m3": E4M3_MAX, "e5m2": E5M2_MAX}
 
 Q, K, V, OUTLIERS, BLOCKS, LENGTHS = range(6)
 
@@ -48,11 +50,11 @@ def with_outliers(x, gen, fraction=0.01, factor=20.0):
     return x
 
 
-def absmax_scales(x):
-    """Per-head scale fl32(max |x[:, h, :]|) / 448 (float32 [H]); 1.0 for an
-    all-zero head."""
+def absmax_scales(x, fmt_max=E4M3_MAX):
+    """Per-head scale fl32(max |x[:, h, :]|) / fmt_max (float32 [H]; fmt_max
+    448 for an e4m3 cache, 57344 for e5m2); 1.0 for an all-zero head."""
     a = np.abs(np.asarray(x, dtype=np.float32)).max(axis=(0, 2))
-    s = (a / np.float32(E4M3_MAX)).astype(np.float32)
+    s = (a / np.float32(fmt_max)).astype(np.float32)
     s[s == 0] = np.float32(1.0)
     return s
 
