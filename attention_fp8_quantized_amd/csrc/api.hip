@@ -295,8 +295,8 @@ fa8_status fa8_prefill_attention(const void* q, const int32_t* cu_q_lens, int32_
     return fail(FA8_EUNSUPPORTED, "prefill: head_dim %d not in {64,128,256}", head_dim);
   if (!fp8_cache(cache_dtype))
     return fail(FA8_EINVAL, "prefill: cache_dtype must be FA8_E4M3 or FA8_E5M2");
-  if (accum_mode != 0 && accum_mode != 1)
-    return fail(FA8_EINVAL, "prefill: accum_mode must be 0 or 1");
+  if (accum_mode < 0 || accum_mode > 65536)
+    return fail(FA8_EINVAL, "prefill: accum_mode must be in 0..65536");
   if (!(std::isfinite(sm_scale)))
     return fail(FA8_EINVAL, "prefill: sm_scale must be finite");
   if (batch == 0 || max_q_len == 0) return ok();

@@ -39,8 +39,15 @@
 //     of 8 key rows; the key order matches the P operand slot by slot;
 //   * P~ . V~ on the FP8 MFMA v_mfma_f32_16x16x128_f8f6f4 (K = the tile's
 //     128 keys).  Level 1: acc = P~ . V~ into a zeroed fp32 accumulator;
-//     level 2: O = alpha*O + acc in VALU fp32 (every tile).  accum_mode = 0
-//     instead lets the MFMA accumulate into alpha*O.
+//     level 2: O = alpha*O + acc in VALU fp32 (every tile).  The level-1
+//     accumulator is one 16-column block at a time (4 registers), so the
+//     flush costs no register file.  accum_mode = 0 instead lets the MFMA
+//     accumulate into alpha*O (one level).  accum_mode = N >= 2 flushes every
+//     N tiles ([BLOG] "大 Head Dimension 的限制" names this as the remedy on
+//     its hardware): a full-width level-1 accumulator acc[D] keeps
+//     acc = alpha*acc + P~.V~ on the MFMA for N tiles, then
+//     O = (product of those alphas)*O + acc; a separate instantiation, so the
+//     extra registers never burden modes 0 and 1.
 // Epilogue: out = O * v_scale / l.
 
 #include <type_traits>
@@ -107,7 +114,7 @@ __device__ __forceinline__ int swz(int r) {
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
-template <int D, int kFmt>
+template <int D, int kFmt, bool kDeferred>
 __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
   constexpr int KQ = D / 32;               // 32-wide chunks of the head dim (bf16 MFMA K)
   constexpr int DB = D / 16;               // 16-wide output column blocks
@@ -185,6 +192,25 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
   f32x4 o[DB];                   // O[query 4g+i][16db + n]
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // flush every N tiles: the full-width level-1 accumulator, the product of
+  // the alphas since the last flush (rows 4g+i), tiles since the last flush
+  f32x4 acc_n[kDeferred ? DB : 1];
+  float acum[4] = {1.f, 1.f, 1.f, 1.f};
+  int since = 0;
+  if constexpr (kDeferred) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc_n[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  auto flush_n = [&]() {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[db][i] = acum[i] * o[db][i] + acc_n[db][i];
+      acc_n[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acum[i] = 1.f;
+  };
 
   // block id of page `page` of the sequence (pages past the end: page 0's;
   // their V rows are zeroed after the copy)
@@ -357,7 +383,25 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
     };
     // software pipeline: the next block's V^T reads are in flight while this
     // block's product runs.  The accumulation mode is tested once per tile.
-    if (p.accum_mode == 1) {
+    if constexpr (kDeferred) {
+      i32x8 vb_next = load_vb(0);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const i32x8 vb = vb_next;
+        if (db + 1 < DB) vb_next = load_vb(db + 1);
+        f32x4 c;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c[i] = alpha_o[i] * acc_n[db][i];
+        acc_n[db] = mfma_pv<kFmt>(pa, vb, c);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acum[i] *= alpha_o[i];
+      if (++since == p.accum_mode) {   // uniform: every lane visits the same tiles
+        flush_n();
+        since = 0;
+      }
+    } else if (p.accum_mode == 1) {
       i32x8 vb_next = load_vb(0);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
@@ -393,6 +437,8 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
     if (t + 1 <= t_hi) tile_step(std::true_type{}, t + 1);
   }
 
+  if constexpr (kDeferred) flush_n();   // the tiles since the last flush
+
   // ---- epilogue: out = O * v_scale / l ---------------------------------------
   const float vsc = p.v_scale[h];
 #pragma unroll
@@ -408,13 +454,19 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
   }
 }
 
-template <int kFmt>
+template <int kFmt, bool kDeferred>
 static hipError_t launch_prefill_f(const PrefillParams& p, dim3 grid, dim3 block,
                                    hipStream_t stream) {
   switch (p.head_dim) {
-    case 64: hipLaunchKernelGGL((prefill_kernel<64, kFmt>), grid, block, 0, stream, p); break;
-    case 128: hipLaunchKernelGGL((prefill_kernel<128, kFmt>), grid, block, 0, stream, p); break;
-    case 256: hipLaunchKernelGGL((prefill_kernel<256, kFmt>), grid, block, 0, stream, p); break;
+    case 64:
+      hipLaunchKernelGGL((prefill_kernel<64, kFmt, kDeferred>), grid, block, 0, stream, p);
+      break;
+    case 128:
+      hipLaunchKernelGGL((prefill_kernel<128, kFmt, kDeferred>), grid, block, 0, stream, p);
+      break;
+    case 256:
+      hipLaunchKernelGGL((prefill_kernel<256, kFmt, kDeferred>), grid, block, 0, stream, p);
+      break;
     default: return hipErrorNotSupported;
   }
   return hipGetLastError();
@@ -423,9 +475,14 @@ static hipError_t launch_prefill_f(const PrefillParams& p, dim3 grid, dim3 block
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   dim3 grid((p.max_q_len + kBlockM - 1) / kBlockM, p.num_q_heads, p.batch);
   dim3 block(64 * kWaves);
+  const bool deferred = p.accum_mode >= 2;
   switch (p.fmt) {
-    case kFmtE4m3: return launch_prefill_f<kFmtE4m3>(p, grid, block, stream);
-    case kFmtE5m2: return launch_prefill_f<kFmtE5m2>(p, grid, block, stream);
+    case kFmtE4m3:
+      return deferred ? launch_prefill_f<kFmtE4m3, true>(p, grid, block, stream)
+                      : launch_prefill_f<kFmtE4m3, false>(p, grid, block, stream);
+    case kFmtE5m2:
+      return deferred ? launch_prefill_f<kFmtE5m2, true>(p, grid, block, stream)
+                      : launch_prefill_f<kFmtE5m2, false>(p, grid, block, stream);
     default: return hipErrorNotSupported;
   }
 }

@@ -143,7 +143,8 @@ def fill_pool(fa, torch, pool_blocks, Hkv, D, cache_dtype, seed, outliers=True):
         v = torch.randn((n, Hkv, D), generator=gen, device=dev) * mul_v
         # the library's on-device scales of this chunk; the scale of the
         # whole pool is the largest chunk scale (the quotient is monotone)
-        cks, cvs = fa.absmax_scales(k, v)
+        cks, cvs = fa.absmax_scales(k, v, cache_dtype=cache_dtype if cache_dtype != "bf16"
+                                    else "e4m3")
         amax_k = torch.maximum(amax_k, cks)
         amax_v = torch.maximum(amax_v, cvs)
     ks = amax_k.contiguous()
@@ -197,7 +198,7 @@ class DecodeLayers:
         self.fa, self.torch = fa, torch
         self.layers, self.lens, self.window = layers, list(lens), window
         self.B, self.Hq, self.Hkv, self.D, self.cd = len(lens), Hq, Hkv, D, cache_dtype
-        self.elem = 1 if cache_dtype == "e4m3" else 2
+        self.elem = 2 if cache_dtype == "bf16" else 1
         pool = pool_blocks_for(layers, self.lens, window)
         self.cache, self.ks, self.vs = fill_pool(fa, torch, pool, Hkv, D, cache_dtype, seed,
                                                  outliers)
@@ -400,7 +401,7 @@ def measure_hd256(fa, torch, reps=3):
     res = {"prefill_32k": []}
     lens = torch.tensor([T], dtype=torch.int32, device=dev)
     fl = prefill_flops(T, 0, Hq, D)
-    for mode in (1, 0):
+    for mode in (1, 0, 2, 4, 8):
         ms = timed(torch, lambda: fa.prefill_attention(q, cu, cache, bt, lens, qs, ks, vs, sm, T,
                                                        accum_mode=mode, out=out), reps)
         tf = fl / (ms * 1e-3) / 1e12
@@ -427,6 +428,45 @@ def measure_hd256(fa, torch, reps=3):
                           "gbs": round(dl.bytes_per_layer / (dec * 1e-3) / 1e9, 1),
                           "splits": dl.S}
     dl.free()
+    return res
+
+
+def measure_e5m2(fa, torch, reps=3):
+    """The e5m2 cache: decode of the 32k Llama-shaped layer (32 distinct
+    layers, decode launches alone) and the causal hd-256 prefill of a 32k
+    chunk (8 q / 1 KV head), next to the same e4m3 runs."""
+    Hq, Hkv, D, ctx = 32, 8, 128, 32768
+    res = {"decode_32k": {}, "prefill_hd256_32k": {}}
+    for cd in ("e5m2", "e4m3"):
+        dl = DecodeLayers(fa, torch, 32, [ctx], Hq, Hkv, D, cd, seed=7000)
+        t = decode_only_ms(torch, dl, reps)
+        gbs = dl.bytes_per_layer / (t * 1e-3) / 1e9
+        res["decode_32k"][cd] = {"us_per_layer": round(t * 1e3, 2), "gbs": round(gbs, 1),
+                                 "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        log(f"  decode 32k {cd}: {t * 1e3:.2f} us/layer, {gbs:.0f} GB/s")
+        dl.free()
+    Hq, Hkv, D, T = 8, 1, 256, 32768
+    dev = torch.device("cuda")
+    gq = torch.Generator(device=dev)
+    gq.manual_seed(7001)
+    q = torch.randn((T, Hq, D), generator=gq, device=dev).to(torch.bfloat16)
+    qs = (q.float().abs().amax() / 448.0).view(1).contiguous()
+    cu = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    lens = torch.tensor([T], dtype=torch.int32, device=dev)
+    out = torch.empty((T, Hq, D), dtype=torch.float32, device=dev)
+    bt = torch.arange(T // 16, dtype=torch.int32, device=dev).view(1, -1)
+    fl = prefill_flops(T, 0, Hq, D)
+    for cd in ("e5m2", "e4m3"):
+        cache, ks, vs = fill_pool(fa, torch, T // 16, Hkv, D, cd, seed=7002, outliers=False)
+        ms = timed(torch, lambda: fa.prefill_attention(q, cu, cache, bt, lens, qs, ks, vs,
+                                                       1.0 / math.sqrt(D), T, out=out), reps)
+        tf = fl / (ms * 1e-3) / 1e12
+        res["prefill_hd256_32k"][cd] = {"ms": round(ms, 4), "tflops": round(tf, 1),
+                                        "frac_fp8_peak": round(tf / FP8_MFMA_PEAK_TFLOPS, 4)}
+        log(f"  prefill hd256 32k {cd}: {ms:.3f} ms, {tf:.0f} TFLOP/s")
+        del cache
+    del q, out
+    torch.cuda.empty_cache()
     return res
 
 
@@ -638,6 +678,8 @@ def main():
         result["hd256"] = measure_hd256(fa, torch)
         log("on-device absmax scales")
         result["absmax_scales"] = measure_absmax(fa, torch)
+        log("e5m2 cache")
+        result["e5m2"] = measure_e5m2(fa, torch)
         if not args.no_cpu:
             log("cpu baseline: oracle decode")
             result["cpu_baseline"] = cpu_baseline(Hq, Hkv, D, ctx)

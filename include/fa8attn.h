@@ -240,7 +240,11 @@ int32_t fa8_prefill_kv_tile(int32_t head_dim);
  *   window     as in decode, counted from each query's own position.
  *   accum_mode 1 = two-level (MFMA sums each KV tile into a zeroed fp32
  *              register tile, then O = alpha*O + tile in fp32; default);
- *              0 = one-level (MFMA accumulates into the rescaled O).
+ *              0 = one-level (MFMA accumulates into the rescaled O);
+ *              N in 2..65536 = flush every N tiles ([BLOG] "大 Head
+ *              Dimension 的限制": a level-1 accumulator spans N tiles, with
+ *              its own alpha rescaling, before O = alpha'*O + acc).  All
+ *              modes compute the same quantity; they differ in rounding.
  *   out        fp32 [total_q][num_q_heads][head_dim].
  * Per row and KV tile t (width fa8_prefill_kv_tile): running max m_t,
  * p = exp(s - m_t) in fp32, P*V uses e4m3(p), the denominator the fp32 p.

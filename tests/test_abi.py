@@ -172,7 +172,8 @@ def test_prefill_rejects_bad_arguments(lib):
 
     assert call(Hq=7) == EINVAL
     assert call(D=80) == EUNSUPPORTED
-    assert call(acc=2) == EINVAL
+    assert call(acc=-1) == EINVAL
+    assert call(acc=65537) == EINVAL
     assert call(cd=1) == EINVAL                  # prefill needs an FP8 cache
     assert call(cd=4) == EINVAL
     assert call(qs=None) == EINVAL

@@ -73,7 +73,7 @@ def test_uniform_scores_mean_of_visible_v():
             assert ma < 1e-5 and rl < 1e-5, (i, hq, ma, rl)
 
 
-@pytest.mark.parametrize("accum_mode", [1, 0])
+@pytest.mark.parametrize("accum_mode", [1, 0, 2, 8])
 def test_hd256_1k_all_rows(accum_mode):
     # 8 q / 1 KV head, head_dim 256, absmax scales (Q per tensor, K/V per head)
     c = PrefillCase([1024], [1024], 8, 1, 256, seed=11)
@@ -90,6 +90,37 @@ def test_hd256_long_chunk_sampled(T):
     got = c.run_gpu()
     ref, slack = c.oracle(rows=rows)
     assert_gate(got[rows], ref, f"hd256 T={T} sampled", slack=slack)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("accum_mode", [2, 3, 16])
+def test_flush_every_n_tiles(D, accum_mode):
+    # flush periods that do and do not divide the tile counts of a ragged
+    # chunked batch (one row sees 1 tile, another 8)
+    c = PrefillCase([130, 100, 17], [130, 1000, 260], 8, 2, D, seed=15)
+    log(f"prefill flush every {accum_mode} tiles D={D}")
+    ref, slack = c.oracle()
+    assert_gate(c.run_gpu(accum_mode), ref, f"flush/{accum_mode} D={D}", slack=slack)
+
+
+def test_accumulation_modes_at_32k():
+    """Every accumulation mode on the 32k hd-256 chunk (sampled rows) passes
+    the same gate; the differences between modes are logged."""
+    T = 32768
+    c = PrefillCase([T], [T], 8, 1, 256, seed=12)
+    rows = _sample_rows(T, 32, seed=3)
+    ref, slack = c.oracle(rows=rows)
+    exact = c.oracle(rows=rows, exact=True)
+    outs = {}
+    for mode in (1, 0, 4, 32):
+        log(f"prefill hd256 T={T} accum_mode={mode}")
+        outs[mode] = c.run_gpu(mode)[rows]
+        assert_gate(outs[mode], ref, f"accum_mode={mode}", slack=slack)
+        ma, rl = metrics(outs[mode], exact)
+        log(f"  vs unquantised-P reference: max_abs={ma:.3e} rel_l2={rl:.3e}")
+    for mode in (0, 4, 32):
+        ma, rl = metrics(outs[mode], outs[1])
+        log(f"  accum_mode={mode} vs 1: max_abs={ma:.3e} rel_l2={rl:.3e}")
 
 
 def test_e5m2_hd256_32k_sampled():
@@ -125,7 +156,7 @@ def test_empty_and_bad_arguments():
     d = c.dev
     with pytest.raises(fa.Fa8Error):
         fa.prefill_attention(c.q_dev, d["cu"], c.cache, d["bt"], d["lens"], d["qs"], d["ks"],
-                             d["vs"], 0.125, 16, accum_mode=3)
+                             d["vs"], 0.125, 16, accum_mode=-1)
     # max_q_len = 0: nothing to do, nothing written
     out = torch.full((16, 2, 64), 7.0, device="cuda")
     fa.prefill_attention(c.q_dev, d["cu"], c.cache, d["bt"], d["lens"], d["qs"], d["ks"],
