@@ -380,7 +380,7 @@ def measure_hybrid(fa, torch, reps=5):
     return res
 
 
-def measure_hd256(fa, torch, reps=3):
+def measure_hd256(fa, torch, reps=3, modes=(1, 0, 2, 4, 8)):
     """8/1 heads, head_dim 256, FP8: causal prefill of a 32k chunk (P = 0,
     accum_mode 1 and 0), a 128k fill in four 32k chunks, and decode at 128k
     over 16 distinct layers."""
@@ -401,7 +401,7 @@ def measure_hd256(fa, torch, reps=3):
     res = {"prefill_32k": []}
     lens = torch.tensor([T], dtype=torch.int32, device=dev)
     fl = prefill_flops(T, 0, Hq, D)
-    for mode in (1, 0, 2, 4, 8):
+    for mode in modes:
         ms = timed(torch, lambda: fa.prefill_attention(q, cu, cache, bt, lens, qs, ks, vs, sm, T,
                                                        accum_mode=mode, out=out), reps)
         tf = fl / (ms * 1e-3) / 1e12
@@ -563,6 +563,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the head_dim-256 leg (prefill + 128k decode); prints its JSON")
+    ap.add_argument("--accum-modes", default="1,0,2,4,8",
+                    help="prefill accumulation modes the head_dim-256 leg times (comma list)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
@@ -574,7 +576,8 @@ def main():
     fa.load()
     torch.cuda.init()
     if args.prefill_only:
-        print(json.dumps({"hd256": measure_hd256(fa, torch)}), flush=True)
+        modes = tuple(int(m) for m in args.accum_modes.split(","))
+        print(json.dumps({"hd256": measure_hd256(fa, torch, modes=modes)}), flush=True)
         return
 
     B, Hq, Hkv, D, ctx, layers = 1, 32, 8, 128, args.ctx, args.layers
@@ -675,7 +678,8 @@ def main():
         log("hybrid")
         result["hybrid"] = measure_hybrid(fa, torch)
         log("head_dim 256")
-        result["hd256"] = measure_hd256(fa, torch)
+        result["hd256"] = measure_hd256(
+            fa, torch, modes=tuple(int(m) for m in args.accum_modes.split(",")))
         log("on-device absmax scales")
         result["absmax_scales"] = measure_absmax(fa, torch)
         log("e5m2 cache")
