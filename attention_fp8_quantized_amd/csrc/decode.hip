@@ -307,35 +307,84 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFmt>())) void decode
   };
 
   // Fused append: the wave that will read the page holding token L-1 encodes
-  // that token's K and V row from the inputs (the same encoder as
-  // cache_write) before its page loop, stores it into the cache and into an
-  // LDS slot of its own, and swaps it in for the row the page load returns.
+  // that token's K and V row from the inputs (the same rounding as
+  // cache_write), stores it into the cache and into an LDS slot of its own,
+  // and swaps it in for the row the page load returns.  Every lane of that
+  // wave takes AE = D/32 consecutive elements of the K row (lanes 0-31) or
+  // the V row (lanes 32-63).  The inputs are loaded here; they are encoded
+  // only after the wave's first page loads are issued, so the owner wave
+  // starts streaming as early as the others.
   const bool append = p.k_new != nullptr && L > 0;
   const int new_page = (L - 1) / kBlockSize;
   const int new_row = (L - 1) % kBlockSize;
   __shared__ __attribute__((aligned(16))) uint8_t s_new[2 * ROW];
   const bool owner = append && new_page >= pg0 && new_page < pg1 && (new_page - pg0) % NW == wave;
-  if (owner && n == new_row) {
-    uint8_t* dst = const_cast<uint8_t*>(head_base) + (size_t)bt[new_page] * blk_stride;
-    const size_t src0 = ((size_t)b * p.num_kv_heads + h) * D;
-    const float ks = kFp8 ? p.k_scale[h] : 1.0f;
-    const float vs = kFp8 ? p.v_scale[h] : 1.0f;
-    for (int hh = 0; hh < NL; ++hh) {
-      const int e0 = kFp8 ? 64 * hh + 16 * g : 32 * hh + 8 * g;   // first element of the piece
-      uint4 kc, vc;
-      if (p.new_bf16) {
-        kc = encode_chunk<true, kFmt>(p.k_new, src0 + e0, ks);
-        vc = encode_chunk<true, kFmt>(p.v_new, src0 + e0, vs);
+  constexpr int AE = D / 32;
+  const int a_kv = lane >> 5;             // 0: K row, 1: V row
+  const int a_e0 = (lane & 31) * AE;      // first element of this lane's piece
+  float a_x[AE];
+  int a_blk = 0;
+  if (owner) {
+    a_blk = bt[new_page];
+    const size_t e = ((size_t)b * p.num_kv_heads + h) * D + a_e0;
+    const void* src = a_kv ? p.v_new : p.k_new;
+    if (p.new_bf16) {
+      const uint16_t* s16 = reinterpret_cast<const uint16_t*>(src) + e;
+      uint32_t w[AE / 2];
+      if constexpr (AE == 2) {
+        w[0] = *reinterpret_cast<const uint32_t*>(s16);
+      } else if constexpr (AE == 4) {
+        const uint2 t = *reinterpret_cast<const uint2*>(s16);
+        w[0] = t.x; w[1] = t.y;
       } else {
-        kc = encode_chunk<false, kFmt>(p.k_new, src0 + e0, ks);
-        vc = encode_chunk<false, kFmt>(p.v_new, src0 + e0, vs);
+        const uint4 t = *reinterpret_cast<const uint4*>(s16);
+        w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
       }
-      *reinterpret_cast<uint4*>(dst + 64 * hh) = kc;
-      *reinterpret_cast<uint4*>(dst + HALF + 64 * hh) = vc;
-      *reinterpret_cast<uint4*>(s_new + 64 * hh + 16 * g) = kc;
-      *reinterpret_cast<uint4*>(s_new + ROW + 64 * hh + 16 * g) = vc;
+#pragma unroll
+      for (int i = 0; i < AE / 2; ++i) {
+        a_x[2 * i] = bf16_lo(w[i]);
+        a_x[2 * i + 1] = bf16_hi(w[i]);
+      }
+    } else {
+      const float* s32 = reinterpret_cast<const float*>(src) + e;
+#pragma unroll
+      for (int i = 0; i < AE; i += 2) {
+        const float2 t = *reinterpret_cast<const float2*>(s32 + i);
+        a_x[i] = t.x;
+        a_x[i + 1] = t.y;
+      }
     }
   }
+  // encode this lane's piece, store it to the cache row and to the LDS slot
+  auto append_row = [&]() {
+    constexpr int PB = AE * ES;           // bytes of the piece: 2 .. 16
+    const float sc = kFp8 ? (a_kv ? p.v_scale[h] : p.k_scale[h]) : 1.0f;
+    uint32_t w[PB >= 4 ? PB / 4 : 1] = {};
+#pragma unroll
+    for (int i = 0; i < AE; ++i) {
+      if constexpr (kFp8) {
+        w[i / 4] |= fp8_encode<kFmt>(a_x[i] / sc) << (8 * (i % 4));
+      } else {
+        w[i / 2] |= bf16_bits(a_x[i]) << (16 * (i % 2));
+      }
+    }
+    uint8_t* dst = const_cast<uint8_t*>(p.cache) + (size_t)a_blk * blk_stride +
+                   (size_t)h * 2 * HALF + a_kv * HALF + new_row * ROW + a_e0 * ES;
+    uint8_t* lds = s_new + a_kv * ROW + a_e0 * ES;
+    if constexpr (PB == 2) {
+      *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w[0];
+      *reinterpret_cast<uint16_t*>(lds) = (uint16_t)w[0];
+    } else if constexpr (PB == 4) {
+      *reinterpret_cast<uint32_t*>(dst) = w[0];
+      *reinterpret_cast<uint32_t*>(lds) = w[0];
+    } else if constexpr (PB == 8) {
+      *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+      *reinterpret_cast<uint2*>(lds) = make_uint2(w[0], w[1]);
+    } else {
+      *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+      *reinterpret_cast<uint4*>(lds) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  };
   auto patch_new_row = [&](Page& pg) {
     if (n != new_row) return;
 #pragma unroll
@@ -481,6 +530,7 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFmt>())) void decode
     Page ring[PD];
 #pragma unroll
     for (int k = 0; k < PD; ++k) issue(ring[k], blk_of(k));
+    if (jb == 0 && owner) append_row();   // before any page is used
     int j = 0;
     for (; j + PD <= cnt; j += PD) {
 #pragma unroll
