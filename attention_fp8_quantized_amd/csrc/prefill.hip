@@ -58,9 +58,7 @@
 namespace fa8 {
 
 constexpr int kTileN = 128;      // keys per KV tile
-constexpr int kWaveRows = 16;    // query rows per wave
-constexpr int kWaves = 8;        // waves per workgroup
-constexpr int kBlockM = kWaveRows * kWaves;
+constexpr int kBlockM = 128;     // query rows per workgroup
 constexpr float kNegInfP = -__builtin_huge_valf();
 
 int prefill_kv_tile(int) { return kTileN; }
@@ -114,15 +112,27 @@ __device__ __forceinline__ int swz(int r) {
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
-template <int D, int kFmt, bool kDeferred>
-__global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
+// s_waitcnt immediate: wait until at most n vector-memory operations are
+// outstanding (lgkm and exp counters not waited on); n up to 63
+constexpr int vmcnt_imm(int n) { return 0x3F70 | (n & 15) | ((n >> 4) << 14); }
+
+// MB = query blocks of 16 rows per wave; the workgroup has 8/MB waves and
+// always 128 query rows.  With MB = 2 each widened K operand and each V^T
+// operand feeds two MFMAs, and a wave owns a SIMD (up to 512 registers).
+template <int D, int kFmt, bool kDeferred, int MB>
+__global__ __launch_bounds__(64 * (8 / MB)) void prefill_kernel(PrefillParams p) {
+  constexpr int NWV = 8 / MB;              // waves per workgroup
   constexpr int KQ = D / 32;               // 32-wide chunks of the head dim (bf16 MFMA K)
   constexpr int DB = D / 16;               // 16-wide output column blocks
   constexpr int TILE = kTileN * D;         // bytes of one staged K (or V) tile
   constexpr int PPT = kTileN / kBlockSize; // pages per tile
   constexpr int RPI = 1024 / D;            // rows per wave-wide 16-byte-per-lane copy
-  constexpr int NCOPY = 2 * TILE / 1024 / kWaves;   // copies per wave per tile
-  static_assert(NCOPY >= 1 && kBlockSize % RPI == 0, "staging tiling");
+  constexpr int CPT = TILE / 1024;         // copies per staged K (or V) tile
+  constexpr int NCOPY = 2 * CPT / NWV;     // copies per wave per tile
+  static_assert(MB == 1 || MB == 2, "query blocks per wave");
+  static_assert(!kDeferred || MB == 1, "flush every N tiles: one query block per wave");
+  static_assert(NCOPY >= 1 && kBlockSize % RPI == 0 && NCOPY + 1 <= 63, "staging tiling");
+  static_assert(16 * MB * NWV == kBlockM, "rows per workgroup");
   // two tile buffers (K then V), filled by direct global->LDS copies while
   // the other one is being computed on
   __shared__ __attribute__((aligned(16))) uint8_t s_buf0[2 * TILE];
@@ -145,33 +155,41 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;                 // lane group (k-slot group of the MFMA)
   const int n = lane & 15;                 // query (S^T, P) or column (V, O) of the lane
-  const int row = q0 + wave * kWaveRows + n;   // this lane's query row (S^T layout)
-  const bool row_ok = row < T;
-  const int pos = P0 + row;
+  const int rbase = q0 + wave * 16 * MB;   // first query row of this wave
+  int row[MB], pos[MB];                    // this lane's query row of block mb (S^T layout)
+  bool row_ok[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    row[mb] = rbase + 16 * mb + n;
+    row_ok[mb] = row[mb] < T;
+    pos[mb] = P0 + row[mb];
+  }
 
   // ---- prologue: quantise this lane's slice of Q (B operand of S^T) ------
   // q8 = e4m3(fl32(q / q_scale)); the operand holds decode(q8) as bf16
-  // (exact); q_scale enters the score multiplier.  Lane (g, n) holds query n,
-  // columns 32*kq + 8*g .. +7 for every chunk kq.
+  // (exact); q_scale enters the score multiplier.  Lane (g, n) holds query n
+  // of each block, columns 32*kq + 8*g .. +7 for every chunk kq.
   const float qsc = p.q_scale[0];
-  bf16x8 qb[KQ];
+  bf16x8 qb[MB][KQ];
 #pragma unroll
-  for (int kq = 0; kq < KQ; ++kq) {
-    uint4 w4 = make_uint4(0, 0, 0, 0);
-    if (row_ok)
-      w4 = *reinterpret_cast<const uint4*>(
-          p.q + ((size_t)(qs + row) * p.num_q_heads + hq) * D + kq * 32 + g * 8);
-    const uint32_t ws[4] = {w4.x, w4.y, w4.z, w4.w};
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int h2 = 0; h2 < 4; ++h2) {
-      const uint32_t c2 = e4m3_encode(bf16_lo(ws[h2]) / qsc) |
-                          (e4m3_encode(bf16_hi(ws[h2]) / qsc) << 8);
-      const bf16x2 d2 = e4m3x2_to_bf16<false>(c2);
-      qb[kq][2 * h2] = d2[0];
-      qb[kq][2 * h2 + 1] = d2[1];
+    for (int kq = 0; kq < KQ; ++kq) {
+      uint4 w4 = make_uint4(0, 0, 0, 0);
+      if (row_ok[mb])
+        w4 = *reinterpret_cast<const uint4*>(
+            p.q + ((size_t)(qs + row[mb]) * p.num_q_heads + hq) * D + kq * 32 + g * 8);
+      const uint32_t ws[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+      for (int h2 = 0; h2 < 4; ++h2) {
+        const uint32_t c2 = e4m3_encode(bf16_lo(ws[h2]) / qsc) |
+                            (e4m3_encode(bf16_hi(ws[h2]) / qsc) << 8);
+        const bf16x2 d2 = e4m3x2_to_bf16<false>(c2);
+        qb[mb][kq][2 * h2] = d2[0];
+        qb[mb][kq][2 * h2 + 1] = d2[1];
+      }
+      __builtin_amdgcn_sched_barrier(0);   // one chunk at a time (register pressure)
     }
-    __builtin_amdgcn_sched_barrier(0);   // one chunk at a time (register pressure)
-  }
   // log2-domain score multiplier
   const float qk = qsc * p.k_scale[h] * p.sm_scale * kLog2e;
 
@@ -187,13 +205,18 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
   const size_t blk_stride = (size_t)p.num_kv_heads * 2 * kBlockSize * D;
 
   // ---- state ----------------------------------------------------------------
-  float m_run = kNegInfP;        // running max of this lane's query (log2 domain)
-  float l_run = 0.f;             // running denominator
-  f32x4 o[DB];                   // O[query 4g+i][16db + n]
+  float m_run[MB], l_run[MB];    // running max (log2 domain) and denominator per block
+  f32x4 o[MB][DB];               // O[query 4g+i of block mb][16db + n]
 #pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // flush every N tiles: the full-width level-1 accumulator, the product of
-  // the alphas since the last flush (rows 4g+i), tiles since the last flush
+  for (int mb = 0; mb < MB; ++mb) {
+    m_run[mb] = kNegInfP;
+    l_run[mb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[mb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // flush every N tiles (MB = 1 only): the full-width level-1 accumulator,
+  // the product of the alphas since the last flush (rows 4g+i), tiles since
+  // the last flush
   f32x4 acc_n[kDeferred ? DB : 1];
   float acum[4] = {1.f, 1.f, 1.f, 1.f};
   int since = 0;
@@ -205,7 +228,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[db][i] = acum[i] * o[db][i] + acc_n[db][i];
+      for (int i = 0; i < 4; ++i) o[0][db][i] = acum[i] * o[0][db][i] + acc_n[db][i];
       acc_n[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
@@ -216,29 +239,32 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
   // their V rows are zeroed after the copy)
   auto page_blk = [&](int page) { return bt[page < n_pages ? page : 0]; };
   // Copy u of this wave (0..NCOPY-1) fills rows row0 .. row0+RPI-1 of the K
-  // (first TILE bytes) or V tile, one 16-byte chunk per lane.  With 8 waves
-  // the row of a lane within its page, and so its swizzle, is the same for
-  // every copy: the per-lane source offset is computed once, and each copy
-  // adds the (uniform) page address.
-  static_assert(kWaves == 8, "copy mapping");
-  const int my_r = (wave * RPI) % kBlockSize + lane / (D / 16);   // row within the page
-  const int my_r16 = (wave * RPI / kBlockSize) & 1;                // bit 4 of the tile row
-  const int lane_off = my_r * D + ((lane % (D / 16)) ^ swz<D>(my_r + 16 * my_r16)) * 16;
+  // (first TILE bytes) or V tile, one 16-byte chunk per lane.  The row of a
+  // lane within its page, and so its swizzle, depends on u at most through
+  // u's parity: the two per-lane source offsets are computed once, and each
+  // copy adds the (uniform) page address.
+  int lane_off[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const int idx = (par % NCOPY) * NWV + wave;
+    const int r = (idx % CPT) * RPI + lane / (D / 16);            // tile row of the lane
+    lane_off[par] = (r % kBlockSize) * D + ((lane % (D / 16)) ^ swz<D>(r)) * 16;
+  }
   auto stage = [&](uint8_t* buf, int slot) {
-    // opaque per call, so that the compiler keeps one 32-bit lane offset and
+    // opaque per call, so that the compiler keeps 32-bit lane offsets and
     // uniform page addresses instead of hoisting a 64-bit address per copy
-    int voff = lane_off;
-    asm volatile("" : "+v"(voff));
+    int voff0 = lane_off[0], voff1 = lane_off[1];
+    asm volatile("" : "+v"(voff0), "+v"(voff1));
 #pragma unroll
     for (int u = 0; u < NCOPY; ++u) {
-      const int idx = u * kWaves + wave;                 // 0 .. 2*TILE/1024-1
-      const int kv = idx / (TILE / 1024);
-      const int row0 = (idx % (TILE / 1024)) * RPI;      // first row (within the tile)
+      const int idx = u * NWV + wave;                    // 0 .. 2*CPT-1
+      const int kv = idx / CPT;
+      const int row0 = (idx % CPT) * RPI;                // first row (within the tile)
       const int blk = __builtin_amdgcn_readfirstlane(s_bt[slot][row0 / kBlockSize]);
       const uint8_t* page = p.cache + (size_t)blk * blk_stride + head_off +
                             (size_t)kv * kBlockSize * D;
-      __builtin_amdgcn_global_load_lds(page + voff, (lds_void_ptr)(buf + kv * TILE + row0 * D), 16,
-                                       0, 0);
+      __builtin_amdgcn_global_load_lds(page + ((u & 1) ? voff1 : voff0),
+                                       (lds_void_ptr)(buf + kv * TILE + row0 * D), 16, 0, 0);
     }
   };
 
@@ -267,39 +293,65 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
     // zero rows, never read), then wait for this tile's copies: everything
     // but the id load and the NCOPY copies just issued
     stage(nxt, (t + 1) & 3);
-    __builtin_amdgcn_s_waitcnt(0x3F70 | (NCOPY + 1));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(NCOPY + 1));
     // rows past the sequence end (the tail tile only): every lane overwrites
     // the V chunks it copied with zeros before the barrier publishes them
     if ((t + 1) * kTileN > L) {
       const int rows_left = L - t * kTileN;
 #pragma unroll
       for (int u = 0; u < NCOPY; ++u) {
-        const int idx = u * kWaves + wave;
-        const int row0 = (idx % (TILE / 1024)) * RPI;
-        if (idx / (TILE / 1024) == 1 && row0 + lane / (D / 16) >= rows_left)
+        const int idx = u * NWV + wave;
+        const int row0 = (idx % CPT) * RPI;
+        if (idx / CPT == 1 && row0 + lane / (D / 16) >= rows_left)
           *reinterpret_cast<uint4*>(cur + TILE + row0 * D + lane * 16) = make_uint4(0, 0, 0, 0);
       }
     }
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     // ---- S^T = K . Q^T : 8 blocks of 16 keys -----------------------------------
-    // the A operand: 8 K codes of key 16 mb + n, columns 32 kq + 8 g,
-    // widened to bf16 (exact)
-    f32x4 s[8];
+    // the A operand: 8 K codes of key 16 kb + n, columns 32 kq + 8 g,
+    // widened to bf16 (exact) once and used for every query block
+    f32x4 s[MB][8];
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) s[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-      const int kr = 16 * mb + n;
+      for (int kb = 0; kb < 8; ++kb) s[mb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // software pipeline over the 8 key blocks: the KQ operand reads of block
+    // kb+1 are issued before block kb's converts and products, so the LDS
+    // round trip hides behind them
+    auto k_reads = [&](uint2 (&ka)[KQ], int kb) {
+      const int kr = 16 * kb + n;
       const uint8_t* krow = s_k + kr * D + 8 * (g & 1);
       const int ksw = swz<D>(kr);
 #pragma unroll
+      for (int kq = 0; kq < KQ; ++kq)
+        ka[kq] = *reinterpret_cast<const uint2*>(krow + (((2 * kq + (g >> 1)) ^ ksw) * 16));
+    };
+    uint2 ka[2][KQ];
+    k_reads(ka[0], 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, KQ, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+      if (kb + 1 < 8) k_reads(ka[(kb + 1) & 1], kb + 1);
+#pragma unroll
       for (int kq = 0; kq < KQ; ++kq) {
-        const uint2 a = *reinterpret_cast<const uint2*>(krow + (((2 * kq + (g >> 1)) ^ ksw) * 16));
+        const uint2 a = ka[kb & 1][kq];
         const bf16x2 a0 = fp8x2_to_bf16<kFmt, false>(a.x), a1 = fp8x2_to_bf16<kFmt, true>(a.x);
         const bf16x2 a2 = fp8x2_to_bf16<kFmt, false>(a.y), a3 = fp8x2_to_bf16<kFmt, true>(a.y);
         const bf16x8 av = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-        s[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[kq], s[mb], 0, 0, 0);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          s[mb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[mb][kq], s[mb][kb], 0, 0, 0);
+      }
+      // instruction order: (4 converts, MB products) per chunk of this block,
+      // with the next block's reads after the first chunk (the wait before
+      // the first chunk then covers only this block's reads)
+#pragma unroll
+      for (int kq = 0; kq < KQ; ++kq) {
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, MB, 0);
+        if (kq == 0 && kb + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, KQ, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -308,55 +360,57 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
     const int k_first = t * kTileN, k_last = k_first + kTileN - 1;
     const bool full = k_last <= P0 + q0 && q0 + kBlockM <= T &&
                       (p.window <= 0 || P0 + rmax - k_first < p.window);
-    float tmax = kNegInfP;
-    if (full) {
+    i32x8 pa[MB];
+    float alpha_o[MB][4];    // alpha of the four queries (4g + i) whose O rows this lane holds
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb)
+    for (int mb = 0; mb < MB; ++mb) {
+      float tmax = kNegInfP;
+      if (full) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          s[mb][i] *= qk;
-          tmax = fmaxf(tmax, s[mb][i]);
-        }
-    } else {
+        for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb)
+          for (int i = 0; i < 4; ++i) {
+            s[mb][kb][i] *= qk;
+            tmax = fmaxf(tmax, s[mb][kb][i]);
+          }
+      } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = k_first + 16 * mb + 4 * g + i;
-          const bool vis = row_ok && key <= pos && (p.window <= 0 || pos - key < p.window);
-          const float v = vis ? s[mb][i] * qk : kNegInfP;
-          s[mb][i] = v;
-          tmax = fmaxf(tmax, v);
-        }
-    }
-    tmax = group4_max(tmax);
-    const float m_new = fmaxf(m_run, tmax);
-    const float ref = m_new > kNegInfP ? m_new : 0.f;
-    const float alpha = m_run > kNegInfP ? fast_exp2(m_run - m_new) : 0.f;
-
-    // ---- probabilities: fp32 sum, e4m3 operand -------------------------------
-    float psum = 0.f;
-    i32x8 pa;
+        for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-      float pv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pv[i] = fast_exp2(s[mb][i] - ref);
-        psum += pv[i];
+          for (int i = 0; i < 4; ++i) {
+            const int key = k_first + 16 * kb + 4 * g + i;
+            const bool vis = row_ok[mb] && key <= pos[mb] &&
+                             (p.window <= 0 || pos[mb] - key < p.window);
+            const float v = vis ? s[mb][kb][i] * qk : kNegInfP;
+            s[mb][kb][i] = v;
+            tmax = fmaxf(tmax, v);
+          }
       }
-      int w = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);  // RNE
-      w = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], w, true);
-      pa[mb] = w;
-    }
-    psum = group4_sum(psum);
-    l_run = alpha * l_run + psum;
-    m_run = m_new;
+      tmax = group4_max(tmax);
+      const float m_new = fmaxf(m_run[mb], tmax);
+      const float ref = m_new > kNegInfP ? m_new : 0.f;
+      const float alpha = m_run[mb] > kNegInfP ? fast_exp2(m_run[mb] - m_new) : 0.f;
 
-    // alpha of the four queries (4g + i) whose O rows this lane holds
-    float alpha_o[4];
+      // ---- probabilities: fp32 sum, e4m3 operand -----------------------------
+      float psum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) alpha_o[i] = __shfl(alpha, 4 * g + i);
+      for (int kb = 0; kb < 8; ++kb) {
+        float pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pv[i] = fast_exp2(s[mb][kb][i] - ref);
+          psum += pv[i];
+        }
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);  // RNE
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], w, true);
+        pa[mb][kb] = w;
+      }
+      psum = group4_sum(psum);
+      l_run[mb] = alpha * l_run[mb] + psum;
+      m_run[mb] = m_new;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) alpha_o[mb][i] = __shfl(alpha, 4 * g + i);
+    }
 
     __builtin_amdgcn_sched_barrier(0);
     // ---- P~ . V~ per 16-column block -------------------------------------------
@@ -382,7 +436,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
       return vb;
     };
     // software pipeline: the next block's V^T reads are in flight while this
-    // block's product runs.  The accumulation mode is tested once per tile.
+    // block's products run.  The accumulation mode is tested once per tile.
     if constexpr (kDeferred) {
       i32x8 vb_next = load_vb(0);
 #pragma unroll
@@ -391,12 +445,12 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
         if (db + 1 < DB) vb_next = load_vb(db + 1);
         f32x4 c;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) c[i] = alpha_o[i] * acc_n[db][i];
-        acc_n[db] = mfma_pv<kFmt>(pa, vb, c);
+        for (int i = 0; i < 4; ++i) c[i] = alpha_o[0][i] * acc_n[db][i];
+        acc_n[db] = mfma_pv<kFmt>(pa[0], vb, c);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acum[i] *= alpha_o[i];
+      for (int i = 0; i < 4; ++i) acum[i] *= alpha_o[0][i];
       if (++since == p.accum_mode) {   // uniform: every lane visits the same tiles
         flush_n();
         since = 0;
@@ -408,9 +462,12 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
         const i32x8 vb = vb_next;
         if (db + 1 < DB) vb_next = load_vb(db + 1);
         // level 1: this tile's P.V into a zeroed accumulator; level 2: fp32 flush
-        const f32x4 acc = mfma_pv<kFmt>(pa, vb, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[db][i] = alpha_o[i] * o[db][i] + acc[i];
+        for (int mb = 0; mb < MB; ++mb) {
+          const f32x4 acc = mfma_pv<kFmt>(pa[mb], vb, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[mb][db][i] = alpha_o[mb][i] * o[mb][db][i] + acc[i];
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
@@ -419,10 +476,13 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
       for (int db = 0; db < DB; ++db) {
         const i32x8 vb = vb_next;
         if (db + 1 < DB) vb_next = load_vb(db + 1);
-        f32x4 c;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) c[i] = alpha_o[i] * o[db][i];
-        o[db] = mfma_pv<kFmt>(pa, vb, c);
+        for (int mb = 0; mb < MB; ++mb) {
+          f32x4 c;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) c[i] = alpha_o[mb][i] * o[mb][db][i];
+          o[mb][db] = mfma_pv<kFmt>(pa[mb], vb, c);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -436,36 +496,44 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
     tile_step(std::false_type{}, t);
     if (t + 1 <= t_hi) tile_step(std::true_type{}, t + 1);
   }
-
   if constexpr (kDeferred) flush_n();   // the tiles since the last flush
 
   // ---- epilogue: out = O * v_scale / l ---------------------------------------
   const float vsc = p.v_scale[h];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float li = __shfl(l_run, 4 * g + i);
-    const int orow = q0 + wave * kWaveRows + 4 * g + i;
-    if (orow < T) {
-      const float sc = li > 0.f ? vsc / li : 0.f;
-      float* dst = p.out + ((size_t)(qs + orow) * p.num_q_heads + hq) * D;
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) dst[16 * db + n] = o[db][i] * sc;
+    for (int i = 0; i < 4; ++i) {
+      const float li = __shfl(l_run[mb], 4 * g + i);
+      const int orow = rbase + 16 * mb + 4 * g + i;
+      if (orow < T) {
+        const float sc = li > 0.f ? vsc / li : 0.f;
+        float* dst = p.out + ((size_t)(qs + orow) * p.num_q_heads + hq) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) dst[16 * db + n] = o[mb][db][i] * sc;
+      }
     }
-  }
 }
 
+#ifndef FA8_PREFILL_MB
+#define FA8_PREFILL_MB 1       // query blocks of 16 rows per wave (1 or 2)
+#endif
+
 template <int kFmt, bool kDeferred>
-static hipError_t launch_prefill_f(const PrefillParams& p, dim3 grid, dim3 block,
-                                   hipStream_t stream) {
+static hipError_t launch_prefill_f(const PrefillParams& p, dim3 grid, hipStream_t stream) {
+  // flush every N tiles keeps one query block per wave (its second
+  // accumulator already fills the registers)
+  constexpr int MB = kDeferred ? 1 : FA8_PREFILL_MB;
+  const dim3 block(64 * (8 / MB));
   switch (p.head_dim) {
     case 64:
-      hipLaunchKernelGGL((prefill_kernel<64, kFmt, kDeferred>), grid, block, 0, stream, p);
+      hipLaunchKernelGGL((prefill_kernel<64, kFmt, kDeferred, MB>), grid, block, 0, stream, p);
       break;
     case 128:
-      hipLaunchKernelGGL((prefill_kernel<128, kFmt, kDeferred>), grid, block, 0, stream, p);
+      hipLaunchKernelGGL((prefill_kernel<128, kFmt, kDeferred, MB>), grid, block, 0, stream, p);
       break;
     case 256:
-      hipLaunchKernelGGL((prefill_kernel<256, kFmt, kDeferred>), grid, block, 0, stream, p);
+      hipLaunchKernelGGL((prefill_kernel<256, kFmt, kDeferred, MB>), grid, block, 0, stream, p);
       break;
     default: return hipErrorNotSupported;
   }
@@ -473,16 +541,15 @@ static hipError_t launch_prefill_f(const PrefillParams& p, dim3 grid, dim3 block
 }
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
-  dim3 grid((p.max_q_len + kBlockM - 1) / kBlockM, p.num_q_heads, p.batch);
-  dim3 block(64 * kWaves);
+  const dim3 grid((p.max_q_len + kBlockM - 1) / kBlockM, p.num_q_heads, p.batch);
   const bool deferred = p.accum_mode >= 2;
   switch (p.fmt) {
     case kFmtE4m3:
-      return deferred ? launch_prefill_f<kFmtE4m3, true>(p, grid, block, stream)
-                      : launch_prefill_f<kFmtE4m3, false>(p, grid, block, stream);
+      return deferred ? launch_prefill_f<kFmtE4m3, true>(p, grid, stream)
+                      : launch_prefill_f<kFmtE4m3, false>(p, grid, stream);
     case kFmtE5m2:
-      return deferred ? launch_prefill_f<kFmtE5m2, true>(p, grid, block, stream)
-                      : launch_prefill_f<kFmtE5m2, false>(p, grid, block, stream);
+      return deferred ? launch_prefill_f<kFmtE5m2, true>(p, grid, stream)
+                      : launch_prefill_f<kFmtE5m2, false>(p, grid, stream);
     default: return hipErrorNotSupported;
   }
 }
