@@ -103,8 +103,8 @@ __device__ __forceinline__ float wave_sum(float v) {
 // kFinal: out[g][d] = v_scale * o / l (0 when every partial is empty);
 // otherwise the merged partial (o, M, l) is stored at row `dst_row` of a
 // block of `dst_rows` rows per head.  All partial loads of a batch (up to
-// kInFlight per thread) are issued before any is used, and the first batch
-// is in flight while the maxima are reduced.
+// 64 per thread) are issued before any is used, and the first batch is in
+// flight while the maxima are reduced.
 template <int D, int GW, int NW, bool kFinal>
 __device__ __forceinline__ void merge_rows(const float* o_in, const float* m_in,
                                            const float* l_in, int rows, int r0, int n,
@@ -114,8 +114,10 @@ __device__ __forceinline__ void merge_rows(const float* o_in, const float* m_in,
   constexpr int COLS = GW * D;                        // output elements
   constexpr int R = NT >= COLS ? NT / COLS : 1;       // threads per output element
   constexpr int EPT = COLS > NT ? COLS / NT : 1;      // output elements per thread
-  constexpr int kInFlight = 32;
-  constexpr int JB = kInFlight / EPT;                 // partial rows per element per batch
+  // partial rows per element per batch: 32 loads in flight per thread for
+  // one element, 16 rows (a whole group of splits) for several, capped at
+  // 64 loads
+  constexpr int JB = EPT == 1 ? 32 : (64 / EPT < 16 ? 64 / EPT : 16);
   constexpr int kMaxRows = kDecodeSingleLevel;
   static_assert(R * COLS == NT || EPT * NT == COLS, "merge tiling");
   __shared__ float s_w[GW][kMaxRows];
@@ -285,7 +287,8 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFmt>())) void decode
 
   // one LDS region: V slices during the loop, the wave merge afterwards
   constexpr int kSliceBytes = kBlockSize * RS;
-  constexpr int kMergeHeads = (32768 / (NW * D * 4)) < G ? (32768 / (NW * D * 4)) : G;
+  // query heads merged per LDS round: all of them within a 64 KB budget
+  constexpr int kMergeHeads = (65536 / (NW * D * 4)) < G ? (65536 / (NW * D * 4)) : G;
   constexpr int kMergeBytes = NW * kMergeHeads * D * 4 + 2 * NW * 16 * 4;
   constexpr int kLdsBytes = NW * kSliceBytes > kMergeBytes ? NW * kSliceBytes : kMergeBytes;
   __shared__ __attribute__((aligned(16))) uint8_t s_raw[kLdsBytes];
