@@ -336,22 +336,35 @@ def measure_slope(fa, torch, Hq, Hkv, D, contexts, min_bytes=1.1e9, reps=3):
 
 def measure_loaded(fa, torch, reps=5):
     """8 sequences of U{18000..22000} tokens, 32/8 heads, hd128, FP8, 32
-    distinct layers back to back (cache write + decode per layer)."""
+    distinct layers back to back: the step with the fused append + decode
+    launch per layer (and with cache_write + decode), decode alone, and a
+    plain streaming read of the same bytes per launch as the yardstick."""
     import workloads as W
     lens = [int(x) for x in W.uniform_lengths(W.rng(3, 0, W.LENGTHS), 8, 18000, 22000)]
     dl = DecodeLayers(fa, torch, 32, lens, 32, 8, 128, "e4m3", seed=3000)
 
     def step():
         for i in range(dl.layers):
+            dl.run_layer_fused(i)
+
+    def step_two_launch():
+        for i in range(dl.layers):
             dl.run_layer(i)
     ms = timed(torch, step, reps)
+    ms2 = timed(torch, step_two_launch, reps)
     dec = decode_only_ms(torch, dl, reps)
     total = dl.layers * (dl.bytes_per_layer + dl.write_bytes)
+    dec_gbs = dl.bytes_per_layer / (dec * 1e-3) / 1e9
     res = {"lens": lens, "layers": 32, "ms_per_step": round(ms, 4),
            "gbs": round(total / (ms * 1e-3) / 1e9, 1),
+           "two_launch_ms_per_step": round(ms2, 4),
            "decode_us_per_layer": round(dec * 1e3, 2),
-           "decode_gbs": round(dl.bytes_per_layer / (dec * 1e-3) / 1e9, 1), "splits": dl.S}
+           "decode_gbs": round(dec_gbs, 1), "splits": dl.S}
+    per = dl.bytes_per_layer
     dl.free()
+    sr = measure_stream_read(fa, torch, per, reps=32)
+    res["stream_read"] = sr
+    res["decode_frac_of_stream_read"] = round(dec_gbs / sr["gbs"], 4)
     return res
 
 

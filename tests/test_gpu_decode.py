@@ -201,3 +201,33 @@ def test_argument_errors_raise():
         # max_seq_len beyond what the block table can address
         fa.decode_attention(c.q_dev, c.cache, c.bt_dev, c.lens_dev, c.ks_dev, c.vs_dev,
                             0.125, 10 ** 6)
+
+
+def test_fused_append_full_size_llama_32k():
+    """The benchmark's step configuration: one 32k-token Llama-shaped layer
+    (32 q / 8 KV heads, head_dim 128, outlier channels), the library's split
+    count.  The fused launch must leave the same cache bytes and the same
+    output as cache_write followed by decode, and match the oracle on two
+    KV heads."""
+    import torch
+    import attention_fp8_quantized_amd as fa
+    L = 32768
+    c = DecodeCase(1, 32, 8, 128, [L], "e4m3", seed=35, outliers=True, skip_last=True,
+                   oracle_heads=[2, 7])
+    k_new = dev(c.k[c.last_idx])
+    v_new = dev(c.v[c.last_idx])
+    slot = int(c.bt[0, (L - 1) // 16]) * 16 + (L - 1) % 16
+    start = c.cache.clone()
+    fa.cache_write(k_new, v_new, dev(np.array([slot], np.int64)), c.ks_dev, c.vs_dev, c.cache)
+    ref_out = c.run_gpu()
+    ref_cache = c.cache.clone()
+    c.cache.copy_(start)
+    log("decode fused append, 32k Llama-shaped layer")
+    out = fa.decode_attention_append(c.q_dev, k_new, v_new, c.cache, c.bt_dev, c.lens_dev,
+                                     c.ks_dev, c.vs_dev, float(c.sm), L)
+    torch.cuda.synchronize()
+    assert torch.equal(c.cache.view(torch.uint8), ref_cache.view(torch.uint8)), "cache bytes"
+    got = out.cpu().numpy()
+    np.testing.assert_array_equal(got, ref_out)
+    ref, qheads = c.oracle()
+    assert_gate(got[:, qheads], ref, "fused append 32k")
