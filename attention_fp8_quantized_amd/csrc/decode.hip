@@ -555,6 +555,7 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFmt>())) void decode
   float* s_m = s_o + NW * kMergeHeads * D;                       // [NW][16]
   float* s_l = s_m + NW * 16;                                    // [NW][16]
   const int S = p.num_splits;
+  const float vsc = p.fp8 ? p.v_scale[h] : 1.0f;
   __shared__ int s_last;
   __syncthreads();            // the V slices are dead from here on
   if (lane < 16) {
@@ -589,16 +590,24 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFmt>())) void decode
           num += f * s_o[(w * kMergeHeads + hd) * D + d];
           den += f * s_l[w * 16 + hq];
         }
-        const size_t row = ((size_t)b * p.num_q_heads + hq0 + hq) * S + split;
-        st_agent(p.ws_o + row * D + d, num);
-        if (d == 0) {
-          st_agent(p.ws_m + row, M);
-          st_agent(p.ws_l + row, den);
+        if (S == 1) {
+          // a single split: this workgroup's state is the whole answer (the
+          // same expression as the split merge's output with one partial)
+          p.out[((size_t)b * p.num_q_heads + hq0 + hq) * D + d] =
+              M > kNegInf ? num * (vsc / den) : 0.f;
+        } else {
+          const size_t row = ((size_t)b * p.num_q_heads + hq0 + hq) * S + split;
+          st_agent(p.ws_o + row * D + d, num);
+          if (d == 0) {
+            st_agent(p.ws_m + row, M);
+            st_agent(p.ws_l + row, den);
+          }
         }
       }
     }
     if (r0 + kMergeHeads < G) __syncthreads();
   }
+  if (S == 1) return;   // no partials, no arrival count, no merge
 
   // ---- the last workgroup of this (sequence, head group) merges the splits -
   // Each thread waits until its partial stores are performed (they are
@@ -621,7 +630,6 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFmt>())) void decode
   __syncthreads();
   if (!s_last) return;
   const size_t head0 = (size_t)b * p.num_q_heads + hq0;   // first query head of the set
-  const float vsc = p.fp8 ? p.v_scale[h] : 1.0f;
   if (NG == 1) {
     merge_rows<D, G, NW, true>(p.ws_o + head0 * S * D, p.ws_m + head0 * S, p.ws_l + head0 * S,
                                 S, 0, S, p.out + head0 * D, nullptr, nullptr, 0, 0, vsc);

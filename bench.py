@@ -368,7 +368,7 @@ def measure_loaded(fa, torch, reps=5):
     return res
 
 
-def measure_hybrid(fa, torch, reps=5):
+def measure_hybrid(fa, torch, reps=20):
     """gpt-oss-20b-shaped step: 24 layers, 12 full-attention and 12
     128-token sliding-window, 64/8 heads, hd64, 8 x 20000 tokens.  Variants:
     all BF16, all FP8, FP8 full layers with BF16 sliding-window layers."""
