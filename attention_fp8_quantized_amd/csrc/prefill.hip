@@ -168,7 +168,10 @@ __global__ __launch_bounds__(64 * (8 / MB)) void prefill_kernel(PrefillParams p)
   // ---- prologue: quantise this lane's slice of Q (B operand of S^T) ------
   // q8 = e4m3(fl32(q / q_scale)); the operand holds decode(q8) as bf16
   // (exact); q_scale enters the score multiplier.  Lane (g, n) holds query n
-  // of each block, columns 32*kq + 8*g .. +7 for every chunk kq.
+  // of each block; MFMA chunk kq takes the head-dim columns
+  // 64*(kq/2) + 16*g + 8*(kq%2) .. +7 (a permutation of the contraction
+  // index, the same for K), so that the K operands of chunks 2m and 2m+1
+  // are one 16-byte run of a key row.
   const float qsc = p.q_scale[0];
   bf16x8 qb[MB][KQ];
 #pragma unroll
@@ -178,7 +181,8 @@ __global__ __launch_bounds__(64 * (8 / MB)) void prefill_kernel(PrefillParams p)
       uint4 w4 = make_uint4(0, 0, 0, 0);
       if (row_ok[mb])
         w4 = *reinterpret_cast<const uint4*>(
-            p.q + ((size_t)(qs + row[mb]) * p.num_q_heads + hq) * D + kq * 32 + g * 8);
+            p.q + ((size_t)(qs + row[mb]) * p.num_q_heads + hq) * D + 64 * (kq / 2) +
+            16 * g + 8 * (kq % 2));
       const uint32_t ws[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
       for (int h2 = 0; h2 < 4; ++h2) {
@@ -316,27 +320,28 @@ __global__ __launch_bounds__(64 * (8 / MB)) void prefill_kernel(PrefillParams p)
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb) s[mb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // software pipeline over the 8 key blocks: the KQ operand reads of block
-    // kb+1 are issued before block kb's converts and products, so the LDS
-    // round trip hides behind them
-    auto k_reads = [&](uint2 (&ka)[KQ], int kb) {
+    // software pipeline over the 8 key blocks: the operand reads of block
+    // kb+1 (one 16-byte read per pair of chunks) are issued after block kb's
+    // first product, so the LDS round trip hides behind the rest
+    auto k_reads = [&](uint4 (&ka)[KQ / 2], int kb) {
       const int kr = 16 * kb + n;
-      const uint8_t* krow = s_k + kr * D + 8 * (g & 1);
+      const uint8_t* krow = s_k + kr * D;
       const int ksw = swz<D>(kr);
 #pragma unroll
-      for (int kq = 0; kq < KQ; ++kq)
-        ka[kq] = *reinterpret_cast<const uint2*>(krow + (((2 * kq + (g >> 1)) ^ ksw) * 16));
+      for (int m = 0; m < KQ / 2; ++m)
+        ka[m] = *reinterpret_cast<const uint4*>(krow + (((4 * m + g) ^ ksw) * 16));
     };
-    uint2 ka[2][KQ];
+    uint4 ka[2][KQ / 2];
     k_reads(ka[0], 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, KQ, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, KQ / 2, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
       if (kb + 1 < 8) k_reads(ka[(kb + 1) & 1], kb + 1);
 #pragma unroll
       for (int kq = 0; kq < KQ; ++kq) {
-        const uint2 a = ka[kb & 1][kq];
+        const uint4 pair = ka[kb & 1][kq / 2];
+        const uint2 a = (kq % 2) ? make_uint2(pair.z, pair.w) : make_uint2(pair.x, pair.y);
         const bf16x2 a0 = fp8x2_to_bf16<kFmt, false>(a.x), a1 = fp8x2_to_bf16<kFmt, true>(a.x);
         const bf16x2 a2 = fp8x2_to_bf16<kFmt, false>(a.y), a3 = fp8x2_to_bf16<kFmt, true>(a.y);
         const bf16x8 av = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
@@ -351,7 +356,7 @@ __global__ __launch_bounds__(64 * (8 / MB)) void prefill_kernel(PrefillParams p)
       for (int kq = 0; kq < KQ; ++kq) {
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, MB, 0);
-        if (kq == 0 && kb + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, KQ, 0);
+        if (kq == 0 && kb + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, KQ / 2, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
