@@ -44,6 +44,10 @@ int kernel_fmt(int32_t dt) {
 }
 bool group_ok(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
 
+// The decode and prefill grids put heads on y and sequences on z, whose
+// extent a launch limits to 65535 workgroups.
+constexpr int kMaxGridYZ = 65535;
+
 int device_cu_count() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
@@ -190,6 +194,8 @@ static fa8_status decode_impl(const void* q, int32_t batch, int32_t num_q_heads,
     return fail(FA8_EINVAL, "decode: sm_scale must be finite");
   if (num_splits < 0 || num_splits > fa8::kDecodeMaxSplits)
     return fail(FA8_EINVAL, "decode: num_splits must be in 0..%d", fa8::kDecodeMaxSplits);
+  if (batch > kMaxGridYZ || num_kv_heads > kMaxGridYZ)
+    return fail(FA8_EUNSUPPORTED, "decode: batch and num_kv_heads must be <= %d", kMaxGridYZ);
   if (batch == 0) return ok();
   if (!q || !cache || !block_table || !seq_lens || !out || !workspace)
     return fail(FA8_EINVAL, "decode: null pointer argument");
@@ -291,6 +297,8 @@ fa8_status fa8_prefill_attention(const void* q, const int32_t* cu_q_lens, int32_
   if (num_q_heads % num_kv_heads != 0)
     return fail(FA8_EINVAL, "prefill: num_q_heads %d not a multiple of num_kv_heads %d",
                 num_q_heads, num_kv_heads);
+  if (batch > kMaxGridYZ || num_q_heads > kMaxGridYZ)
+    return fail(FA8_EUNSUPPORTED, "prefill: batch and num_q_heads must be <= %d", kMaxGridYZ);
   if (!head_dim_ok(head_dim))
     return fail(FA8_EUNSUPPORTED, "prefill: head_dim %d not in {64,128,256}", head_dim);
   if (!fp8_cache(cache_dtype))

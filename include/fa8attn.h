@@ -32,8 +32,9 @@
  *   Dequantised value = scale * decode(code).  Scales must be finite and
  *   positive (not checked on the device).
  * - Errors: host-side checks return FA8_EINVAL (bad argument) or
- *   FA8_EUNSUPPORTED (valid but not built, e.g. head_dim 96) before anything
- *   is launched; a failed launch returns FA8_EHIP.  fa8_last_error() gives a
+ *   FA8_EUNSUPPORTED (valid but not built, e.g. head_dim 96, or a batch or
+ *   head count above 65535 for decode and prefill) before anything is
+ *   launched; a failed launch returns FA8_EHIP.  fa8_last_error() gives a
  *   message for the calling thread.  Indices that only the device sees
  *   (slot ids, block ids, sequence lengths) are preconditions: out-of-range
  *   values are undefined behaviour.

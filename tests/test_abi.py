@@ -132,6 +132,8 @@ def test_decode_rejects_bad_arguments(lib):
     assert _decode(lib, sm=float("inf")) == EINVAL
     assert _decode(lib, splits=-1) == EINVAL
     assert _decode(lib, splits=257) == EINVAL
+    assert _decode(lib, B=65536) == EUNSUPPORTED             # grid z extent
+    assert _decode(lib, B=65535, wsb=100) == EINVAL          # ...65535 passes that check
     assert _decode(lib, B=0) == 0                            # empty batch: no-op
 
 
@@ -177,6 +179,8 @@ def test_prefill_rejects_bad_arguments(lib):
     assert call(cd=1) == EINVAL                  # prefill needs an FP8 cache
     assert call(cd=4) == EINVAL
     assert call(qs=None) == EINVAL
+    assert call(B=65536) == EUNSUPPORTED         # grid z extent
+    assert call(Hq=65536 * 2, Hkv=2) == EUNSUPPORTED   # grid y extent
     assert call(B=0) == 0
 
 
