@@ -96,30 +96,72 @@ __device__ __forceinline__ float wave_sum(float v) {
   return cross_rows_sum(group_sum<16>(v));
 }
 
+// 16-byte workspace accesses with the cache policy the compiler gives
+// agent-scope atomic loads and stores (sc1): coherent across the L2 caches
+// like ld_agent / st_agent, but one memory request per four floats.  A
+// merger's partials stream through one CU, whose request rate bounds it.
+constexpr int kScopeAgent = 16;                 // cache-policy bits: sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ws_rsrc(const float* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, (int)bytes, 0x00020000);
+}
+// V consecutive floats (V = 1, 2 or 4) in the low lanes of an f32x4
+template <int V>
+__device__ __forceinline__ f32x4 ld_agentv(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  if constexpr (V == 4) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kScopeAgent));
+  } else if constexpr (V == 2) {
+    const f32x2 x = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, kScopeAgent));
+    return f32x4{x[0], x[1], 0.f, 0.f};
+  } else {
+    return f32x4{__builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, kScopeAgent)),
+                 0.f, 0.f, 0.f};
+  }
+}
+template <int V>
+__device__ __forceinline__ void st_agentv(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f32x4 v) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  if constexpr (V == 4) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, byte_off, 0, kScopeAgent);
+  } else if constexpr (V == 2) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, f32x2{v[0], v[1]}), r, byte_off, 0,
+                                          kScopeAgent);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, v[0]), r, byte_off, 0, kScopeAgent);
+  }
+}
+// Floats per workspace access: the widest that still gives every thread of
+// a workgroup of nt threads its own group of columns (cols outputs), so that
+// the merges keep all threads busy and issue the fewest requests.
+constexpr int ws_vec(int cols, int nt) { return cols >= 4 * nt ? 4 : cols >= 2 * nt ? 2 : 1; }
+
 // Merge n unnormalised partials (o, m, l) of each of GW query heads, run by
 // one workgroup.  Head g's partial rows are rows r0 .. r0+n-1 of a block of
 // `rows` rows starting at (head g) * rows:
 //   M = max_i m_i,  w_i = 2^(m_i - M),  o = sum_i w_i o_i,  l = sum_i w_i l_i.
 // kFinal: out[g][d] = v_scale * o / l (0 when every partial is empty);
 // otherwise the merged partial (o, M, l) is stored at row `dst_row` of a
-// block of `dst_rows` rows per head.  All partial loads of a batch (up to
-// 64 per thread) are issued before any is used, and the first batch is in
-// flight while the maxima are reduced.
+// block of `dst_rows` rows per head.  Each thread owns V consecutive
+// columns (one load of V floats per partial row); R adjacent lanes share
+// them and take every R-th row.  All partial loads of a batch are issued before
+// any is used, and the first batch is in flight while the maxima are
+// reduced.
 template <int D, int GW, int NW, bool kFinal>
 __device__ __forceinline__ void merge_rows(const float* o_in, const float* m_in,
                                            const float* l_in, int rows, int r0, int n,
                                            float* o_dst, float* m_dst, float* l_dst,
                                            int dst_rows, int dst_row, float vsc) {
   constexpr int NT = 64 * NW;
-  constexpr int COLS = GW * D;                        // output elements
-  constexpr int R = NT >= COLS ? NT / COLS : 1;       // threads per output element
-  constexpr int EPT = COLS > NT ? COLS / NT : 1;      // output elements per thread
-  // partial rows per element per batch: 32 loads in flight per thread for
-  // one element, 16 rows (a whole group of splits) for several, capped at
-  // 64 loads
-  constexpr int JB = EPT == 1 ? 32 : (64 / EPT < 16 ? 64 / EPT : 16);
+  constexpr int V = ws_vec(GW * D, NT);               // columns per load
+  constexpr int C4 = GW * D / V;                      // V-column groups of the output
+  constexpr int R = NT >= C4 ? NT / C4 : 1;           // threads per group
+  constexpr int EPT = C4 > NT ? C4 / NT : 1;          // groups per thread
+  // partial rows per thread per batch: 32 four-byte or 16 wider loads in
+  // flight for one group, 8 rows for several
+  constexpr int JB = EPT > 1 ? 8 : V == 1 ? 32 : 16;
   constexpr int kMaxRows = kDecodeSingleLevel;
-  static_assert(R * COLS == NT || EPT * NT == COLS, "merge tiling");
+  static_assert(R * C4 == NT || EPT * NT == C4, "merge tiling");
+  static_assert(R <= 64, "a group's threads are lanes of one wave");
   __shared__ float s_w[GW][kMaxRows];
   __shared__ float s_l[GW][kMaxRows];
   __shared__ float s_mx[GW];
@@ -129,17 +171,18 @@ __device__ __forceinline__ void merge_rows(const float* o_in, const float* m_in,
   const int wave = t >> 6;
   const int col0 = t / R;
   const int r = t % R;
+  const __amdgpu_buffer_rsrc_t src = ws_rsrc(o_in, (uint32_t)(GW * rows * D * 4));
 
-  float v[EPT][JB];
+  f32x4 v[EPT][JB];
   auto issue = [&](int j0) {
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
       const int col = col0 + e * (NT / R);
-      const float* src = o_in + ((size_t)(col / D) * rows + r0) * D + col % D;
+      const uint32_t base = (uint32_t)((col / (D / V)) * rows + r0) * D + (col % (D / V)) * V;
 #pragma unroll
       for (int j = 0; j < JB; ++j) {
         const int i = min(j0 + r + j * R, n - 1);   // rows past n repeat row n-1, weight 0
-        v[e][j] = ld_agent(src + (size_t)i * D);
+        v[e][j] = ld_agentv<V>(src, (base + (uint32_t)i * D) * 4);
       }
     }
   };
@@ -182,34 +225,41 @@ __device__ __forceinline__ void merge_rows(const float* o_in, const float* m_in,
     }
   }
   __syncthreads();
-  float acc[EPT];
+  f32x4 acc[EPT];
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) acc[e] = 0.f;
+  for (int e = 0; e < EPT; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int j0 = 0; j0 < n; j0 += JB * R) {
     if (j0 > 0) issue(j0);
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
-      const int g = (col0 + e * (NT / R)) / D;
+      const int g = (col0 + e * (NT / R)) / (D / V);
 #pragma unroll
       for (int j = 0; j < JB; ++j) {
         const int i = j0 + r + j * R;
-        if (i < n) acc[e] += s_w[g][i] * v[e][j];
+        if (i < n) {
+          const float w = s_w[g][i];
+#pragma unroll
+          for (int c = 0; c < V; ++c) acc[e][c] += w * v[e][j][c];
+        }
       }
     }
   }
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
-    float a = acc[e];
-    a = group_sum<R>(a);   // the R threads of an element are adjacent lanes
+    f32x4 a = acc[e];
+#pragma unroll
+    for (int c = 0; c < V; ++c) a[c] = group_sum<R>(a[c]);   // the R threads are adjacent lanes
     const int col = col0 + e * (NT / R);
-    const int g = col / D;
-    const int d = col % D;
+    const int g = col / (D / V);
+    const int d = (col % (D / V)) * V;
     if (r == 0) {
       if constexpr (kFinal) {
-        o_dst[(size_t)g * D + d] = s_mx[g] > kNegInf ? a * (vsc / s_den[g]) : 0.f;
+        const float f = vsc / s_den[g];
+#pragma unroll
+        for (int c = 0; c < V; ++c) o_dst[(size_t)g * D + d + c] = s_mx[g] > kNegInf ? a[c] * f : 0.f;
       } else {
-        const size_t row = (size_t)g * dst_rows + dst_row;
-        st_agent(o_dst + row * D + d, a);
+        const int row = g * dst_rows + dst_row;
+        st_agentv<V>(ws_rsrc(o_dst, (uint32_t)(GW * dst_rows * D * 4)), (uint32_t)(row * D + d) * 4, a);
         if (d == 0) {
           st_agent(m_dst + row, s_mx[g]);
           st_agent(l_dst + row, s_den[g]);
@@ -574,33 +624,42 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFmt>())) void decode
           s_o[(wave * kMergeHeads + hd) * D + 16 * c + n] = o[c][i];
       }
     __syncthreads();
-    for (int t = threadIdx.x; t < kMergeHeads * D; t += 64 * NW) {
-      const int hd = t / D;
-      const int d = t % D;
+    // VW consecutive columns per thread, one partial store each
+    constexpr int VW = ws_vec(kMergeHeads * D, 64 * NW);
+    for (int t = threadIdx.x; t < kMergeHeads * D / VW; t += 64 * NW) {
+      const int hd = t / (D / VW);
+      const int d = (t % (D / VW)) * VW;
       const int hq = r0 + hd;
       if (hq < G) {
         float M = kNegInf;
 #pragma unroll
         for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w * 16 + hq]);
-        float num = 0.f, den = 0.f;
+        f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
+        float den = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
           const float mw = s_m[w * 16 + hq];
           const float f = mw > kNegInf ? fast_exp2(mw - M) : 0.f;
-          num += f * s_o[(w * kMergeHeads + hd) * D + d];
+#pragma unroll
+          for (int c = 0; c < VW; ++c) num[c] += f * s_o[(w * kMergeHeads + hd) * D + d + c];
           den += f * s_l[w * 16 + hq];
         }
         if (S == 1) {
           // a single split: this workgroup's state is the whole answer (the
           // same expression as the split merge's output with one partial)
-          p.out[((size_t)b * p.num_q_heads + hq0 + hq) * D + d] =
-              M > kNegInf ? num * (vsc / den) : 0.f;
+          const float f = vsc / den;
+#pragma unroll
+          for (int c = 0; c < VW; ++c)
+            p.out[((size_t)b * p.num_q_heads + hq0 + hq) * D + d + c] = M > kNegInf ? num[c] * f : 0.f;
         } else {
-          const size_t row = ((size_t)b * p.num_q_heads + hq0 + hq) * S + split;
-          st_agent(p.ws_o + row * D + d, num);
+          // this set's partial rows: [G heads][S splits][D] from head hq0
+          const int row = hq * S + split;
+          st_agentv<VW>(ws_rsrc(p.ws_o + ((size_t)b * p.num_q_heads + hq0) * S * D, (uint32_t)(G * S * D * 4)),
+                    (uint32_t)(row * D + d) * 4, num);
           if (d == 0) {
-            st_agent(p.ws_m + row, M);
-            st_agent(p.ws_l + row, den);
+            const size_t mrow = ((size_t)b * p.num_q_heads + hq0 + hq) * S + split;
+            st_agent(p.ws_m + mrow, M);
+            st_agent(p.ws_l + mrow, den);
           }
         }
       }
