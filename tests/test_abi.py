@@ -78,8 +78,10 @@ def test_num_splits_bounds(lib):
     assert lib.fa8_decode_num_splits(1, 8, 0, 0) == 1
     s = lib.fa8_decode_num_splits(1, 8, 32768, 0)
     assert 1 <= s <= 256
-    # at least 8 pages per split
+    # at least 8 pages (one per wave) per split
     assert lib.fa8_decode_num_splits(1, 8, 64, 0) == 1
+    assert lib.fa8_decode_num_splits(1, 1, 16 * 16, 0) == 2
+    assert lib.fa8_decode_num_splits(1, 1, 16 * 15, 0) == 1
     # a 128-token window never needs more than ceil(128/16)+1 pages
     assert lib.fa8_decode_num_splits(8, 8, 20000, 128) <= 2
 
