@@ -55,7 +55,7 @@ FP8_MFMA_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, TFLOP/s
 # HBM traffic of the decode kernel, measured with hardware counters; valid
 # only while the decode sources hash to the value recorded beside it
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_llama_ctx32k_traffic.md")
-DECODE_SOURCES = ["decode.hip", "fa8_device.hpp", "fa8_internal.hpp"]
+DECODE_SOURCES = ["decode.hip", "fa8_device.hpp", "fa8_internal.hpp", "api.hip"]
 
 
 def log(msg):
