@@ -96,10 +96,10 @@ __device__ __forceinline__ float wave_sum(float v) {
   return cross_rows_sum(group_sum<16>(v));
 }
 
-// 16-byte workspace accesses with the cache policy the compiler gives
-// agent-scope atomic loads and stores (sc1): coherent across the L2 caches
-// like ld_agent / st_agent, but one memory request per four floats.  A
-// merger's partials stream through one CU, whose request rate bounds it.
+// Workspace accesses of 4, 8 or 16 bytes with the cache policy the compiler
+// gives agent-scope atomic loads and stores (sc1): coherent across the L2
+// caches like ld_agent / st_agent, but up to four floats per memory request.
+// A merger's partials stream through one CU, whose request rate can bound it.
 constexpr int kScopeAgent = 16;                 // cache-policy bits: sc1
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t ws_rsrc(const float* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, (int)bytes, 0x00020000);
@@ -143,8 +143,8 @@ constexpr int ws_vec(int cols, int nt) { return cols >= 4 * nt ? 4 : cols >= 2 *
 // otherwise the merged partial (o, M, l) is stored at row `dst_row` of a
 // block of `dst_rows` rows per head.  Each thread owns V consecutive
 // columns (one load of V floats per partial row); R adjacent lanes share
-// them and take every R-th row.  All partial loads of a batch are issued before
-// any is used, and the first batch is in flight while the maxima are
+// them and take every R-th row.  All partial loads of a batch are issued
+// before any is used, and the first batch is in flight while the maxima are
 // reduced.
 template <int D, int GW, int NW, bool kFinal>
 __device__ __forceinline__ void merge_rows(const float* o_in, const float* m_in,
@@ -153,14 +153,14 @@ __device__ __forceinline__ void merge_rows(const float* o_in, const float* m_in,
                                            int dst_rows, int dst_row, float vsc) {
   constexpr int NT = 64 * NW;
   constexpr int V = ws_vec(GW * D, NT);               // columns per load
-  constexpr int C4 = GW * D / V;                      // V-column groups of the output
-  constexpr int R = NT >= C4 ? NT / C4 : 1;           // threads per group
-  constexpr int EPT = C4 > NT ? C4 / NT : 1;          // groups per thread
+  constexpr int CG = GW * D / V;                      // V-column groups of the output
+  constexpr int R = NT >= CG ? NT / CG : 1;           // threads per group
+  constexpr int EPT = CG > NT ? CG / NT : 1;          // groups per thread
   // partial rows per thread per batch: 32 four-byte or 16 wider loads in
   // flight for one group, 8 rows for several
   constexpr int JB = EPT > 1 ? 8 : V == 1 ? 32 : 16;
   constexpr int kMaxRows = kDecodeSingleLevel;
-  static_assert(R * C4 == NT || EPT * NT == C4, "merge tiling");
+  static_assert(R * CG == NT || EPT * NT == CG, "merge tiling");
   static_assert(R <= 64, "a group's threads are lanes of one wave");
   __shared__ float s_w[GW][kMaxRows];
   __shared__ float s_l[GW][kMaxRows];
