@@ -79,6 +79,25 @@ def test_split_count_invariance(cd):
         assert rl < tol, (s, rl)
 
 
+@pytest.mark.parametrize("D,G", [(256, 4), (128, 8), (64, 16), (256, 16), (128, 16)])
+def test_two_level_merge_access_widths(D, G):
+    # The merges move partials 4, 8 or 16 bytes per lane, chosen from the
+    # G*D outputs of a (sequence, KV head) set: 8 bytes for G*D = 1024,
+    # 16 bytes for 2048, and 16 bytes with two column groups per thread for
+    # 4096.  Beyond 64 splits the merge runs in two levels; with 250 splits
+    # the shorter sequence leaves most splits empty.
+    c = DecodeCase(2, 2 * G, 2, D, [3000, 1777], "e4m3", seed=40 + D + G)
+    ref, qheads = c.oracle()
+    one = c.run_gpu(num_splits=1)
+    assert_gate(one[:, qheads], ref, f"D={D} G={G} splits=1")
+    for s in [100, 250]:
+        log(f"decode D={D} G={G} splits={s}")
+        got = c.run_gpu(num_splits=s)
+        assert_gate(got[:, qheads], ref, f"D={D} G={G} splits={s}")
+        ma, rl = metrics(got, one)
+        assert rl < 6e-4, (s, rl)
+
+
 @pytest.mark.parametrize("cd", ["e4m3", "e5m2", "bf16"])
 @pytest.mark.parametrize("window", [0, 100])
 def test_stale_nan_rows_past_sequence_end(cd, window):
