@@ -268,6 +268,26 @@ def timed(torch, fn, reps):
     return e0.elapsed_time(e1) / reps
 
 
+def graph_timed(torch, fn, reps):
+    """Average ms of one replay of a HIP graph that captured fn(): the host
+    path of every launch (Python, ctypes, the HIP runtime) is paid once, at
+    capture, as in a serving engine's graph-captured decode loop.  fn runs
+    once on the capture stream first (torch's capture rule)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    ms = timed(torch, g.replay, reps)
+    del g
+    return ms
+
+
 def decode_only_ms(torch, dl, reps):
     """Per-layer ms of decode alone, cycling through the distinct layers."""
     def all_layers():
@@ -313,20 +333,33 @@ def measure_slope(fa, torch, Hq, Hkv, D, contexts, min_bytes=1.1e9, reps=3):
     last-level cache cannot serve them.  Returns times, slopes, ratio."""
     res = {}
     for cd, elem in (("e4m3", 1), ("bf16", 2)):
-        times = []
+        times, eager = [], []
         for ctx in contexts:
             per = decode_bytes(1, Hq, Hkv, D, ctx, elem)
             layers = int(min(256, max(4, math.ceil(min_bytes / per))))
             dl = DecodeLayers(fa, torch, layers, [ctx], Hq, Hkv, D, cd, seed=2000 + ctx + elem)
-            t = decode_only_ms(torch, dl, reps=max(1, reps * 32 // layers))
+            r = max(1, reps * 32 // layers)
+            te = decode_only_ms(torch, dl, reps=r)
+
+            def all_layers():
+                for i in range(dl.layers):
+                    dl.run_layer(i, write=False)
+            t = graph_timed(torch, all_layers, r) / dl.layers
             times.append(t)
-            log(f"  slope point {cd} ctx={ctx}: {t * 1e3:.2f} us/layer "
+            eager.append(te)
+            log(f"  slope point {cd} ctx={ctx}: {t * 1e3:.2f} us/layer graph, {te * 1e3:.2f} eager "
                 f"({per / t / 1e6:.0f} GB/s, S={dl.S}, {layers} layers)")
             dl.free()
         s, i = slope_fit(contexts, times)
+        se, ie = slope_fit(contexts, eager)
         res[cd] = dict(ms_per_layer=[round(x, 6) for x in times], slope_ms_per_token=s,
-                       intercept_ms=i)
+                       intercept_ms=i, eager_ms_per_layer=[round(x, 6) for x in eager],
+                       eager_slope_ms_per_token=se, eager_intercept_ms=ie)
+    res["timing"] = ("ms_per_layer: one HIP graph replay of the distinct layers' decode launches "
+                     "/ layers; eager_*: the same launches issued one by one from Python")
     res["ratio_fp8_over_bf16"] = res["e4m3"]["slope_ms_per_token"] / res["bf16"]["slope_ms_per_token"]
+    res["eager_ratio_fp8_over_bf16"] = (res["e4m3"]["eager_slope_ms_per_token"] /
+                                        res["bf16"]["eager_slope_ms_per_token"])
     s8, i8 = res["e4m3"]["slope_ms_per_token"], res["e4m3"]["intercept_ms"]
     s16, i16 = res["bf16"]["slope_ms_per_token"], res["bf16"]["intercept_ms"]
     res["break_even_tokens"] = (i8 - i16) / (s16 - s8) if s16 != s8 else None
@@ -370,8 +403,11 @@ def measure_loaded(fa, torch, reps=5):
 
 def measure_hybrid(fa, torch, reps=20):
     """gpt-oss-20b-shaped step: 24 layers, 12 full-attention and 12
-    128-token sliding-window, 64/8 heads, hd64, 8 x 20000 tokens.  Variants:
-    all BF16, all FP8, FP8 full layers with BF16 sliding-window layers."""
+    128-token sliding-window, 64/8 heads, hd64, 8 x 20000 tokens, one fused
+    append + decode launch per layer.  Variants: all BF16, all FP8, FP8 full
+    layers with BF16 sliding-window layers.  ms_per_step: one HIP graph
+    replay of the step (a sliding-window launch is shorter than the eager
+    host path of a launch); eager_ms_per_step: launches issued from Python."""
     lens = [20000] * 8
     res = {}
     for name, full_cd, sw_cd in (("all-bf16", "bf16", "bf16"), ("all-fp8", "e4m3", "e4m3"),
@@ -381,13 +417,15 @@ def measure_hybrid(fa, torch, reps=20):
 
         def step():
             for i in range(12):
-                sw.run_layer(i)
-                full.run_layer(i)
-        ms = timed(torch, step, reps)
+                sw.run_layer_fused(i)
+                full.run_layer_fused(i)
+        eager = timed(torch, step, reps)
+        ms = graph_timed(torch, step, reps)
         total = 12 * (full.bytes_per_layer + full.write_bytes + sw.bytes_per_layer +
                       sw.write_bytes)
-        res[name] = {"ms_per_step": round(ms, 4), "gbs": round(total / (ms * 1e-3) / 1e9, 1)}
-        log(f"  hybrid {name}: {ms:.3f} ms/step")
+        res[name] = {"ms_per_step": round(ms, 4), "gbs": round(total / (ms * 1e-3) / 1e9, 1),
+                     "eager_ms_per_step": round(eager, 4)}
+        log(f"  hybrid {name}: {ms:.3f} ms/step graph, {eager:.3f} eager")
         full.free()
         sw.free()
     return res
@@ -648,6 +686,8 @@ def main():
     dec_ms = e0.elapsed_time(e1) / n_launch
     # the same step as two launches per layer (cache_write, then decode)
     two_ms = timed(torch, step_two_launch, args.steps)
+    graph_ms = graph_timed(torch, step, args.steps)
+    log(f"step as one HIP graph replay: {graph_ms:.4f} ms")
     log(f"two-launch step: {two_ms:.4f} ms")
 
     step_bytes = layers * (dl.bytes_per_layer + dl.write_bytes)
@@ -675,6 +715,7 @@ def main():
                 "scales, device RNG",
         "step": {"kernels": "decode_attention_append per layer (the current token's cache "
                             "write fused into the decode launch)",
+                 "graph_ms_per_step": round(graph_ms, 5),
                  "two_launch_ms_per_step": round(two_ms, 5),
                  "two_launch_value": round(step_bytes / (two_ms * 1e-3) / 1e9, 2)},
         "config": {"workload": "Llama-3.1-8B-shaped FP8 decode step, 32 distinct layers",
