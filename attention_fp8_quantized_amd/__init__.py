@@ -91,18 +91,31 @@ def _check(status):
         raise Fa8Error(status, lib.fa8_last_error().decode())
 
 
+_torch_mod = None
+
+
 def _torch():
-    import torch
-    return torch
+    global _torch_mod
+    if _torch_mod is None:
+        import torch
+        _torch_mod = torch
+    return _torch_mod
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # ctypes takes a plain int for a c_void_p argument
+    return None if t is None else t.data_ptr()
 
 
 def _stream(t):
+    """The current stream of t's device as an integer handle.  torch's raw
+    accessor skips building a Stream object (about 2 us per call); the
+    public call is the fallback."""
     torch = _torch()
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(t.device.index if t.device.index is not None else torch.cuda.current_device())
+    return torch.cuda.current_stream(t.device).cuda_stream
 
 
 def _require(t, name, dtype=None, device=None, ndim=None):
@@ -215,8 +228,17 @@ def decode_num_splits(batch, num_kv_heads, max_seq_len, window=0):
     return int(load().fa8_decode_num_splits(batch, num_kv_heads, max_seq_len, window))
 
 
+_ws_bytes = {}
+
+
 def decode_workspace_bytes(batch, num_q_heads, head_dim, num_splits):
-    return int(load().fa8_decode_workspace_bytes(batch, num_q_heads, head_dim, num_splits))
+    key = (batch, num_q_heads, head_dim, num_splits)
+    n = _ws_bytes.get(key)
+    if n is None:
+        n = int(load().fa8_decode_workspace_bytes(batch, num_q_heads, head_dim, num_splits))
+        if len(_ws_bytes) < 4096:
+            _ws_bytes[key] = n
+    return n
 
 
 def new_decode_workspace(nbytes, device="cuda"):
