@@ -204,3 +204,31 @@ def test_absmax_scales_rejects_bad_arguments(lib):
     assert call(ks=None) == EINVAL
     assert call(k=None) == EINVAL
     assert call(n=-1) == EINVAL
+
+
+def test_missing_library_raises_and_nothing_falls_back(monkeypatch, tmp_path):
+    # with no library every call raises: there is no host implementation
+    monkeypatch.setattr(fa, "_lib", None)
+    monkeypatch.setattr(fa, "library_path", lambda: str(tmp_path / "absent.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        fa.load()
+    with pytest.raises(RuntimeError):
+        fa.decode_num_splits(1, 8, 1024)
+    with pytest.raises(RuntimeError):
+        fa.prefill_kv_tile(128)
+
+
+def test_host_tensors_are_rejected(lib):
+    # the binding passes device pointers only; host tensors are refused before
+    # any call into the library
+    torch = pytest.importorskip("torch")
+    cache = torch.zeros((4, 2, 2, 16, 64), dtype=torch.uint8)
+    q = torch.zeros((1, 8, 64), dtype=torch.bfloat16)
+    bt = torch.zeros((1, 4), dtype=torch.int32)
+    lens = torch.ones(1, dtype=torch.int32)
+    sc = torch.ones(2, dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa.decode_attention(q, cache, bt, lens, sc, sc, 0.125, 16, num_splits=1)
+    k = torch.zeros((3, 2, 64), dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa.cache_write(k, k, torch.zeros(3, dtype=torch.int64), sc, sc, cache)
