@@ -626,6 +626,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the head_dim-256 leg (prefill + 128k decode); prints its JSON")
+    ap.add_argument("--hybrid-only", action="store_true",
+                    help="only the gpt-oss-20b-shaped hybrid leg; prints its JSON")
     ap.add_argument("--accum-modes", default="1,0,2,4,8",
                     help="prefill accumulation modes the head_dim-256 leg times (comma list)")
     args = ap.parse_args()
@@ -641,6 +643,9 @@ def main():
     if args.prefill_only:
         modes = tuple(int(m) for m in args.accum_modes.split(","))
         print(json.dumps({"hd256": measure_hd256(fa, torch, modes=modes)}), flush=True)
+        return
+    if args.hybrid_only:
+        print(json.dumps({"hybrid": measure_hybrid(fa, torch)}), flush=True)
         return
 
     B, Hq, Hkv, D, ctx, layers = 1, 32, 8, 128, args.ctx, args.layers
