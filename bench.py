@@ -558,6 +558,39 @@ def measure_absmax(fa, torch, reps=10):
     return res
 
 
+def measure_cache_write_bulk(fa, torch, reps=10):
+    """Bulk cache write of a 128k-token Llama-shaped layer (131072 x 8 x 128
+    k and v rows) into an e4m3 cache through a permuted slot mapping (every
+    page a different physical block): fp32 and bf16 rows.  HBM-bound: the
+    rows are read once and the codes written once."""
+    n, h, d = 131072, 8, 128
+    nb = n // 16
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(6100)
+    perm = torch.randperm(nb, generator=torch.Generator().manual_seed(6101)).cuda()
+    slots = (perm.repeat_interleave(16) * 16 + torch.arange(16, device="cuda").repeat(nb)).to(torch.int64)
+    cache = fa.new_cache(nb, h, d, "e4m3")
+    ks = torch.ones(h, device="cuda")
+    vs = torch.ones(h, device="cuda")
+    res = {}
+    for name, dt in (("f32", torch.float32), ("bf16", torch.bfloat16)):
+        k = torch.randn((n, h, d), generator=gen, device="cuda").to(dt)
+        v = torch.randn((n, h, d), generator=gen, device="cuda").to(dt)
+        fa.absmax_scales(k, v, ks, vs)
+        ms = timed(torch, lambda: fa.cache_write(k, v, slots, ks, vs, cache), reps)
+        nbytes = cache_write_bytes(n, h, d, k.element_size(), 1)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"bytes": nbytes, "us": round(ms * 1e3, 2), "gbs": round(gbs, 1),
+                     "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        log(f"  cache_write bulk {name}: {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
+        del k, v
+    del cache
+    torch.cuda.empty_cache()
+    res["workload"] = ("k and v rows of a 131072-token layer, 8 KV heads, head_dim 128, into "
+                       "an e4m3 cache, permuted pages")
+    return res
+
+
 def cpu_baseline(Hq, Hkv, D, ctx, budget_s=10.0):
     """The fp64 oracle decoding one Llama-shaped layer at ``ctx`` on the host
     (bounded sample: one layer, repeated until ``budget_s`` of CPU time)."""
@@ -753,6 +786,7 @@ def main():
             fa, torch, modes=tuple(int(m) for m in args.accum_modes.split(",")))
         log("on-device absmax scales")
         result["absmax_scales"] = measure_absmax(fa, torch)
+        result["cache_write_bulk"] = measure_cache_write_bulk(fa, torch)
         log("e5m2 cache")
         result["e5m2"] = measure_e5m2(fa, torch)
         if not args.no_cpu:
