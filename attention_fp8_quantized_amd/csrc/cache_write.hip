@@ -19,7 +19,10 @@
 
 namespace fa8 {
 
-template <bool kInBf16, int kFmt>
+// kIdx: the integer type of the chunk index (uint32_t whenever the chunk
+// count fits, so the index splits into (token, head, chunk) with 32-bit
+// divisions instead of 64-bit ones).
+template <bool kInBf16, int kFmt, typename kIdx>
 __global__ __launch_bounds__(256) void cache_write_kernel(
     const void* __restrict__ k, const void* __restrict__ v, int64_t n_tokens,
     int num_kv_heads, int head_dim, const int64_t* __restrict__ slot_mapping,
@@ -34,12 +37,13 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
   const void* src = which ? v : k;
   const float* scale = which ? v_scale : k_scale;
 
-  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
-       t += (int64_t)gridDim.x * blockDim.x) {
-    const int c = (int)(t % chunks_per_row);
-    const int64_t rest = t / chunks_per_row;
-    const int h = (int)(rest % num_kv_heads);
-    const int64_t n = rest / num_kv_heads;
+  const kIdx cpr = (kIdx)chunks_per_row, nkv = (kIdx)num_kv_heads;
+  for (kIdx t = (kIdx)blockIdx.x * blockDim.x + threadIdx.x; t < (kIdx)total;
+       t += (kIdx)gridDim.x * blockDim.x) {
+    const int c = (int)(t % cpr);
+    const kIdx rest = t / cpr;
+    const int h = (int)(rest % nkv);
+    const int64_t n = (int64_t)(rest / nkv);
     const int64_t slot = slot_mapping[n];
     if (slot < 0) continue;  // padding row
 
@@ -67,9 +71,17 @@ hipError_t launch_cache_write(const void* k, const void* v, bool in_bf16,
   if (blocks > 65535) blocks = 65535;  // grid-stride loop covers the rest
   dim3 grid((unsigned)blocks, 2);
   uint8_t* c = reinterpret_cast<uint8_t*>(cache);
-#define FA8_CW(BF, FMT)                                                                     \
-  hipLaunchKernelGGL((cache_write_kernel<BF, FMT>), grid, threads, 0, stream, k, v, n_tokens, \
-                     num_kv_heads, head_dim, slot_mapping, k_scale, v_scale, c)
+  // the grid-stride index stays below total + gridDim.x * blockDim.x
+  const bool idx32 = total + (int64_t)blocks * threads < ((int64_t)1 << 32);
+#define FA8_CW(BF, FMT)                                                                       \
+  do {                                                                                        \
+    if (idx32)                                                                                \
+      hipLaunchKernelGGL((cache_write_kernel<BF, FMT, uint32_t>), grid, threads, 0, stream, k, \
+                         v, n_tokens, num_kv_heads, head_dim, slot_mapping, k_scale, v_scale, c); \
+    else                                                                                      \
+      hipLaunchKernelGGL((cache_write_kernel<BF, FMT, uint64_t>), grid, threads, 0, stream, k, \
+                         v, n_tokens, num_kv_heads, head_dim, slot_mapping, k_scale, v_scale, c); \
+  } while (0)
   switch (fmt) {
     case kFmtE4m3: if (in_bf16) FA8_CW(true, kFmtE4m3); else FA8_CW(false, kFmtE4m3); break;
     case kFmtE5m2: if (in_bf16) FA8_CW(true, kFmtE5m2); else FA8_CW(false, kFmtE5m2); break;
