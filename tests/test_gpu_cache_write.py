@@ -2,7 +2,7 @@
 
 e4m3 / e5m2 cache: code = fp8(fl32(x / scale[h])) with round-to-nearest-even
 and saturation; bf16 cache: bf16 rounding of x.  Checked exhaustively over every
-bf16 bit pattern at three scales, on random fp32 at several magnitudes, on an
+bf16 bit pattern at four scales, on random fp32 at several magnitudes, on an
 edge set (ties, saturation, inf, NaN, fp32 subnormals, signed zeros), through
 both input dtypes, and with a sentinel-filled cache to prove that only the
 mapped slots change.
@@ -58,8 +58,12 @@ def _all_bf16_as_f32():
 
 
 @pytest.mark.parametrize("cd", ["e4m3", "e5m2"])
-@pytest.mark.parametrize("scale", [1.0, 0.0123, 2.0 ** -5])
+@pytest.mark.parametrize("scale", [1.0, 0.0123, 2.0 ** -5, 7.0])
 def test_exhaustive_bf16_patterns(scale, cd):
+    # at s = 7 the correctly rounded x / s and x * fl32(1 / s) encode 60 of
+    # the bf16 patterns differently in each format (tests/golden/
+    # quantize_division.txt works three of them by hand), so the K rows
+    # compare the division itself
     Hkv, D = 2, 128
     x = _all_bf16_as_f32().reshape(-1, Hkv, D)             # 256 tokens
     v = -x[::-1].copy()

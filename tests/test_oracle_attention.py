@@ -79,6 +79,45 @@ def test_cache_write_scale_divides():
     assert e4m3.decode(c2[0, 0, 1, 0, 0]) == 0.75     # 3 / 4
 
 
+def _division_golden():
+    rows = []
+    for line in open(os.path.join(GOLDEN, "quantize_division.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        fmt, rest = line.split(None, 1)
+        *xe, se, code = rest.split()
+        rows.append((fmt, np.float32(eval(" ".join(xe))), np.float32(float(se)), int(code, 16)))
+    return rows
+
+
+def _quantize_by_reciprocal(x, s, fmt):
+    """A plausible wrong reading: multiply by the fp32 reciprocal of the
+    scale instead of dividing by it."""
+    r = np.float32(np.float32(1.0) / np.float32(s))
+    y = np.multiply(np.float32(x), r, dtype=np.float32)
+    return (e4m3.encode(y) if fmt == "e4m3" else e5m2.encode(y))
+
+
+def test_quantize_rows_divides_correctly_rounded():
+    # hand-worked rows on FP8 rounding midpoints (tests/golden/quantize_division.txt)
+    rows = _division_golden()
+    assert len(rows) >= 3
+    separating = 0
+    for fmt, x, s, code in rows:
+        got = int(Qn.quantize_rows(np.array([x]), s, fmt)[0])
+        assert got == code, (fmt, float(x), float(s), hex(got), hex(code))
+        # the same value through the cache write, as a K row of head 0
+        c = Qn.new_cache(1, 1, 1, fmt)
+        Qn.cache_write(c, np.array([[[x]]]), np.array([[[x]]]), np.array([3]),
+                       np.array([s]), np.array([s]), fmt)
+        assert c[0, 0, 0, 3, 0] == code and c[0, 0, 1, 3, 0] == code
+        if int(_quantize_by_reciprocal(x, s, fmt)) != code:
+            separating += 1
+    # the reciprocal-multiply reading fails every midpoint row at s = 7
+    assert separating == sum(1 for r in rows if r[2] == np.float32(7.0)) >= 3
+
+
 def test_e5m2_cache_write_layout_and_scale():
     Hkv, D = 2, 4
     cache = Qn.new_cache(3, Hkv, D, "e5m2", fill=0xA5)
@@ -284,6 +323,66 @@ def test_mirror_tiny_worked_example():
     got_x = A.mirror_row(s, keys, V, ex["kv_tile"], quantize_p=False)[0]
     assert got_q == pytest.approx(eval(ex["expected_quantized"]), rel=1e-15)
     assert got_x == pytest.approx(eval(ex["expected_exact"]), rel=1e-15)
+
+
+def _window_relative_mirror(s, keys, V, kv_tile, quantize_p=True):
+    """A plausible wrong reading: tiles counted from the first visible key."""
+    return A.mirror_row(s, keys - keys[0], V, kv_tile, quantize_p)
+
+
+def test_mirror_windowed_rows_use_absolute_tiles():
+    # hand-worked rows whose first visible key is not tile-aligned
+    # (tests/golden/prefill_mirror_window.json), including the kernel's
+    # 128-key tile width
+    with open(os.path.join(GOLDEN, "prefill_mirror_window.json")) as f:
+        ex = json.load(f)
+    s = np.array([eval(x, {"math": math}) for x in ex["scores"]])
+    V = np.array(ex["values"])[:, None]
+    want_q = eval(ex["expected_quantized"])
+    want_rel = eval(ex["expected_window_relative_tiles"])
+    assert abs(want_q - want_rel) > 1e-3
+    for case in ex["cases"]:
+        keys = np.array(case["keys"])
+        bn = case["kv_tile"]
+        assert keys[0] % bn != 0
+        assert A.mirror_row(s, keys, V, bn)[0] == pytest.approx(want_q, rel=1e-14)
+        assert A.recurrence_row(s, keys, V, bn) == pytest.approx(np.array([want_q]), rel=1e-14)
+        assert A.mirror_row(s, keys, V, bn, quantize_p=False)[0] == pytest.approx(
+            eval(ex["expected_exact"]), rel=1e-14)
+        # the window-relative reading lands on the other value, so it fails
+        rel = _window_relative_mirror(s, keys, V, bn)[0]
+        assert rel == pytest.approx(want_rel, rel=1e-14)
+        assert rel != pytest.approx(want_q, rel=1e-6)
+
+
+def test_windowed_prefill_mirror_passes_absolute_key_positions():
+    # through the whole reference (cache, block table, masks): every row of a
+    # windowed chunk equals mirror_row over its visible keys at their absolute
+    # positions; with the window start inside a tile, tiles counted from the
+    # window start give a different result for some row
+    kv_tile = 16
+    c = _case(B=1, Hq=2, Hkv=1, D=64, lens=(90,), seed=21)
+    q = W.bf16_values(W.normal(np.random.default_rng(5), (40, 2, 64)))[1]
+    cu = np.array([0, 40], np.int32)
+    qs = np.float32(np.abs(q).max() / 448.0)
+    sm = np.float32(0.125)
+    window = 37                                    # starts are not 16-aligned
+    out = A.prefill_mirror(q, cu, c["cache"], c["bt"], c["lens"], qs, c["ks"], c["vs"],
+                           sm, window, kv_tile)
+    K, Vv = A.gather_kv(c["cache"], c["bt"][0], 0, 90, 0, "e4m3", c["ks"], c["vs"])
+    qhat = A.quantize_query(q, qs)
+    differs = 0
+    for r in range(40):
+        pos = 50 + r
+        lo, hi = A.visible_range(pos, window)
+        keys = np.arange(lo, hi)
+        for hq in range(2):
+            sc = np.float64(sm) * (qhat[r, hq] @ K[lo:hi].T)
+            want = A.mirror_row(sc, keys, Vv[lo:hi], kv_tile)
+            np.testing.assert_allclose(out[r, hq], want, rtol=0, atol=1e-13)
+            wrong = _window_relative_mirror(sc, keys, Vv[lo:hi], kv_tile)
+            differs += int(np.max(np.abs(wrong - want)) > 1e-9)
+    assert differs > 0
 
 
 @pytest.mark.parametrize("kv_tile", [2, 16, 64])
