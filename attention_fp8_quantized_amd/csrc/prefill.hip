@@ -239,9 +239,14 @@ __global__ __launch_bounds__(64 * (8 / MB)) void prefill_kernel(PrefillParams p)
     for (int i = 0; i < 4; ++i) acum[i] = 1.f;
   };
 
-  // block id of page `page` of the sequence (pages past the end: page 0's;
-  // their V rows are zeroed after the copy)
-  auto page_blk = [&](int page) { return bt[page < n_pages ? page : 0]; };
+  // Block id of page `page` of the sequence.  Only the entries of pages
+  // pg_lo .. n_pages-1 are ever read: pg_lo holds the first key any row of
+  // this block can see, so entries outside the window (a freed page, -1) are
+  // never dereferenced.  A staged tile that reaches below pg_lo or past the
+  // end copies the nearest visible page instead; those rows are masked in
+  // the scores and their V rows zeroed after the copy.
+  const int pg_lo = lo_key / kBlockSize;
+  auto page_blk = [&](int page) { return bt[min(max(page, pg_lo), n_pages - 1)]; };
   // Copy u of this wave (0..NCOPY-1) fills rows row0 .. row0+RPI-1 of the K
   // (first TILE bytes) or V tile, one 16-byte chunk per lane.  The row of a
   // lane within its page, and so its swizzle, depends on u at most through
@@ -298,16 +303,21 @@ __global__ __launch_bounds__(64 * (8 / MB)) void prefill_kernel(PrefillParams p)
     // but the id load and the NCOPY copies just issued
     stage(nxt, (t + 1) & 3);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(NCOPY + 1));
-    // rows past the sequence end (the tail tile only): every lane overwrites
-    // the V chunks it copied with zeros before the barrier publishes them
-    if ((t + 1) * kTileN > L) {
-      const int rows_left = L - t * kTileN;
+    // V rows no row of this block can see: past the sequence end (the tail
+    // tile) or before the first visible key (the first tile of a windowed
+    // block).  They hold another page's rows or whatever a stale page held,
+    // and P = 0 times NaN would be NaN, so every lane overwrites the V chunks
+    // it copied there with zeros before the barrier publishes them.
+    if ((t + 1) * kTileN > L || t * kTileN < lo_key) {
+      const int rows_lo = lo_key - t * kTileN;
+      const int rows_hi = L - t * kTileN;
 #pragma unroll
       for (int u = 0; u < NCOPY; ++u) {
         const int idx = u * NWV + wave;
-        const int row0 = (idx % CPT) * RPI;
-        if (idx / CPT == 1 && row0 + lane / (D / 16) >= rows_left)
-          *reinterpret_cast<uint4*>(cur + TILE + row0 * D + lane * 16) = make_uint4(0, 0, 0, 0);
+        const int r = (idx % CPT) * RPI + lane / (D / 16);
+        if (idx / CPT == 1 && (r < rows_lo || r >= rows_hi))
+          *reinterpret_cast<uint4*>(cur + TILE + (r - lane / (D / 16)) * D + lane * 16) =
+              make_uint4(0, 0, 0, 0);
       }
     }
     __builtin_amdgcn_s_barrier();

@@ -151,6 +151,13 @@ size_t fa8_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
  *   q            bf16 [batch][num_q_heads][head_dim]; query head hq reads
  *                KV head hq / (num_q_heads / num_kv_heads).
  *   block_table  int32 [batch][max_blocks_per_seq] physical block ids.
+ *                Only the entries of pages that hold a visible key are read:
+ *                pages lo/16 .. (seq_lens[b]-1)/16 with lo the first key of
+ *                the window (0 without one).  Entries outside the window may
+ *                hold anything (a freed page, -1), and the cache rows of
+ *                invisible keys (also the rows of a visible page before lo or
+ *                past the end) may hold any bytes, NaN codes included: they
+ *                never reach the output.
  *   seq_lens     int32 [batch]; the query is token seq_lens[b]-1, whose K/V
  *                must already be in the cache.  0 gives a zero output row.
  *   max_seq_len  host upper bound of seq_lens (sizes the grid only).
@@ -234,6 +241,13 @@ int32_t fa8_prefill_kv_tile(int32_t head_dim);
  *   seq_lens   int32 [batch]: context length INCLUDING this chunk; the
  *              chunk's queries sit at positions seq_len - q_len .. seq_len-1
  *              and their K/V must already be in the cache.
+ *   block_table  int32 [batch][max_blocks_per_seq].  Only the entries of
+ *              pages lo/16 .. (seq_len-1)/16 are read, lo being the first
+ *              key the chunk's first query sees (its position - window + 1,
+ *              at least 0; 0 without a window).  Entries outside that range
+ *              may hold anything (a freed page, -1), and cache rows no query
+ *              sees (before a window start, past the end) may hold any
+ *              bytes, NaN codes included: they never reach the output.
  *   q_scale    fp32 [1] device: q8 = e4m3(fl32(q / q_scale)) (the query is
  *              e4m3 whatever the cache's FP8 format).
  *   cache_dtype  FA8_E4M3 or FA8_E5M2: the format of K and V codes.  P is

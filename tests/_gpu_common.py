@@ -5,7 +5,9 @@ library's own cache_write, the CPU side builds its cache with the oracle.
 Nothing computed on the GPU is fed to the oracle.
 """
 
+import json
 import math
+import os
 import sys
 
 import numpy as np
@@ -34,16 +36,50 @@ def metrics(gpu, ref):
     return max_abs, rel
 
 
-def assert_gate(gpu, ref, what, max_abs=MAX_ABS, rel_l2=REL_L2, slack=None):
+def worst_row(gpu, ref):
+    """(relative L2, index) of the output row (last axis) with the largest
+    relative L2 error; rows whose reference is 0 count their absolute norm."""
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if gpu.size == 0:
+        return 0.0, ()
+    d = np.linalg.norm(gpu - ref, axis=-1)
+    n = np.linalg.norm(ref, axis=-1)
+    r = np.where(n > 0, d / np.where(n > 0, n, 1.0), d)
+    i = np.unravel_index(int(np.argmax(r)), r.shape)
+    return float(r[i]), tuple(int(x) for x in i)
+
+
+def record(entry):
+    """Append one parity result to the JSON-lines file named by
+    FA8_PARITY_LOG (nothing when it is unset)."""
+    path = os.environ.get("FA8_PARITY_LOG")
+    if not path:
+        return
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+    with open(path, "a") as f:
+        f.write(json.dumps(entry) + "\n")
+
+
+def assert_gate(gpu, ref, what, max_abs=MAX_ABS, rel_l2=REL_L2, slack=None, meta=None):
     """Gate: relative L2 of the raw difference, and max |gpu - ref| beyond
     ``slack`` (the oracle's per-element allowance for e4m3 roundings of p
-    that a float32 kernel may legitimately take the other way; None = 0)."""
+    that a float32 kernel may legitimately take the other way; None = 0).
+    ``meta`` (kernel, shape, context, mode, ...) goes into the parity record
+    with the measured errors."""
     ma, rl = metrics(gpu, ref)
     diff = np.abs(np.asarray(gpu, np.float64) - np.asarray(ref, np.float64))
     excess = diff if slack is None else np.maximum(diff - slack, 0.0)
     me = float(excess.max()) if excess.size else 0.0
+    wr, wi = worst_row(gpu, ref)
     extra = "" if slack is None else f" beyond-flip-allowance={me:.3e} (max allowance {float(np.max(slack)):.3e})"
-    log(f"  {what}: max_abs={ma:.3e} rel_l2={rl:.3e}{extra}")
+    log(f"  {what}: max_abs={ma:.3e} rel_l2={rl:.3e} worst_row_rel_l2={wr:.3e}{extra}")
+    rec = dict(what=what, max_abs=ma, rel_l2=rl, excess=me, worst_row_rel_l2=wr,
+               worst_row=list(wi), elements=int(diff.size),
+               finite=bool(np.all(np.isfinite(gpu))),
+               passed=bool(me <= max_abs and rl <= rel_l2 and np.all(np.isfinite(gpu))))
+    rec.update(meta or {})
+    record(rec)
     assert np.all(np.isfinite(gpu)), f"{what}: non-finite GPU output"
     assert me <= max_abs and rl <= rel_l2, f"{what}: max_abs={ma:.3e} excess={me:.3e} rel_l2={rl:.3e}"
 
@@ -62,7 +98,7 @@ class DecodeCase:
 
     def __init__(self, B, Hq, Hkv, D, lens, cache_dtype="e4m3", seed=0,
                  outliers=False, scales="absmax", window=0, oracle_heads=None,
-                 q_zero=False, fill=0, skip_last=False):
+                 q_zero=False, fill=0, skip_last=False, window_only=False):
         import torch
         import attention_fp8_quantized_amd as fa
         self.B, self.Hq, self.Hkv, self.D = B, Hq, Hkv, D
@@ -84,6 +120,21 @@ class DecodeCase:
         else:
             self.ks = self.vs = np.ones(Hkv, dtype=np.float32)
         self.slots = W.all_slots(self.bt, self.lens)
+        # window_only: only the keys the window shows are written, and the
+        # table entries of pages wholly before the window name one extra
+        # block that is never written (it keeps the fill bytes, NaN codes
+        # with fill=0xFF): nothing outside the window may reach the output
+        self.visible = np.ones(N, dtype=bool)
+        if window_only:
+            assert window > 0
+            sentinel = self.nblocks
+            self.nblocks += 1
+            at = 0
+            for b, L in enumerate(self.lens):
+                lo = max(0, int(L) - window)
+                self.visible[at:at + lo] = False
+                self.bt[b, :lo // 16] = sentinel
+                at += int(L)
         # host-side bounds checks before anything is launched
         need = W.blocks_needed(self.lens)
         for b, n in enumerate(need):
@@ -102,7 +153,7 @@ class DecodeCase:
         # decode token, to be appended by the caller)
         ends = np.cumsum(self.lens) - 1
         self.last_idx = ends[self.lens > 0]
-        write = np.ones(N, dtype=bool)
+        write = self.visible.copy()
         if skip_last:
             write[self.last_idx] = False
         if write.any():
@@ -159,7 +210,7 @@ class PrefillCase:
     by cu)."""
 
     def __init__(self, qlens, lens, Hq, Hkv, D, seed=0, window=0, q_zero=False,
-                 q_scale="absmax", fill=0, cache_dtype="e4m3"):
+                 q_scale="absmax", fill=0, cache_dtype="e4m3", window_only=False):
         import torch
         import attention_fp8_quantized_amd as fa
         self.qlens = np.asarray(qlens, dtype=np.int32)
@@ -176,6 +227,20 @@ class PrefillCase:
         fm = W.FMT_MAX[cache_dtype]
         self.ks, self.vs = W.absmax_scales(k, fm), W.absmax_scales(v, fm)
         self.slots = W.all_slots(self.bt, self.lens)
+        # window_only: only keys some query of the chunk can see are written
+        # (from the first query's window start on); the table entries of
+        # pages wholly before it name one extra block that is never written
+        self.write = np.ones(N, dtype=bool)
+        if window_only:
+            assert window > 0
+            sentinel = self.nblocks
+            self.nblocks += 1
+            at = 0
+            for b, (L, T) in enumerate(zip(self.lens, self.qlens)):
+                lo = max(0, int(L) - int(T) - window + 1)
+                self.write[at:at + lo] = False
+                self.bt[b, :lo // 16] = sentinel
+                at += int(L)
         need = W.blocks_needed(self.lens)
         for b, nb in enumerate(need):
             assert np.all((self.bt[b, :nb] >= 0) & (self.bt[b, :nb] < self.nblocks))
@@ -191,7 +256,9 @@ class PrefillCase:
         self.k, self.v = k, v
         self.cache = fa.new_cache(self.nblocks, Hkv, D, cache_dtype)
         self.cache.view(torch.uint8).fill_(fill)
-        fa.cache_write(dev(k), dev(v), dev(self.slots), dev(self.ks), dev(self.vs), self.cache)
+        w = self.write
+        fa.cache_write(dev(k[w]), dev(v[w]), dev(self.slots[w]), dev(self.ks), dev(self.vs),
+                       self.cache)
         self.q_dev = qb.cuda()
         self.dev = {n: dev(a) for n, a in dict(cu=self.cu, bt=self.bt, lens=self.lens,
                                                 qs=self.qs, ks=self.ks, vs=self.vs).items()}
@@ -211,8 +278,9 @@ class PrefillCase:
     def oracle_cache(self):
         if self._oracle_cache is None:
             c = OQ.new_cache(self.nblocks, self.Hkv, self.D, self.cd)
-            self._oracle_cache = OQ.cache_write(c, self.k, self.v, self.slots, self.ks, self.vs,
-                                                self.cd)
+            w = self.write
+            self._oracle_cache = OQ.cache_write(c, self.k[w], self.v[w], self.slots[w], self.ks,
+                                                self.vs, self.cd)
         return self._oracle_cache
 
     # float32 score and exp2 error of the kernel, relative, with a 4x margin

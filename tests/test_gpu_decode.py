@@ -16,11 +16,11 @@ from _gpu_common import DecodeCase, assert_gate, dev, log, metrics
 pytestmark = pytest.mark.gpu
 
 
-def _check(case, what, **kw):
+def _check(case, what, meta=None, **kw):
     log(f"decode {what}")
     got = case.run_gpu(**kw)
     ref, qheads = case.oracle()
-    assert_gate(got[:, qheads], ref, what)
+    assert_gate(got[:, qheads], ref, what, meta=meta)
     return got
 
 
@@ -37,7 +37,9 @@ def test_llama_shaped_layer(ctx, cd):
     # scales (absmax/448 for e4m3, absmax/57344 for e5m2)
     heads = None if ctx <= 32768 else [0, 5]
     c = DecodeCase(1, 32, 8, 128, [ctx], cd, seed=2, outliers=True, oracle_heads=heads)
-    _check(c, f"llama-shaped ctx={ctx} {cd}")
+    _check(c, f"llama-shaped ctx={ctx} {cd}",
+           meta=dict(kernel="decode", shape="32/8 hd128 batch 1", context=ctx, cache=cd,
+                     compared=f"KV heads {heads or 'all'}"))
 
 
 @pytest.mark.parametrize("D", [64, 128, 256])
@@ -102,10 +104,25 @@ def test_two_level_merge_access_widths(D, G):
 @pytest.mark.parametrize("window", [0, 100])
 def test_stale_nan_rows_past_sequence_end(cd, window):
     # pages are pre-filled with NaN codes; the rows past each sequence end
-    # (and before the window start) keep them and must not reach the output
+    # keep them and must not reach the output (rows before a window start:
+    # test_out_of_window_pages_never_used)
     lens = [1000, 37, 5, 129]
     c = DecodeCase(len(lens), 16, 2, 128, lens, cd, seed=33, window=window, fill=0xFF)
     got = _check(c, f"stale NaN rows {cd} window={window}")
+    assert np.all(np.isfinite(got))
+
+
+@pytest.mark.parametrize("cd", ["e4m3", "e5m2", "bf16"])
+@pytest.mark.parametrize("window", [100, 128, 513])
+def test_out_of_window_pages_never_used(window, cd):
+    # the cache starts as NaN codes and only the keys inside each window are
+    # written: the rows before the window start in its first page keep NaN,
+    # and the table entries of pages wholly before the window name a block
+    # that is never written (valid memory full of NaN codes)
+    lens = [1000, 37, 5, 129, 2000]
+    c = DecodeCase(len(lens), 16, 2, 128, lens, cd, seed=50 + window, window=window,
+                   fill=0xFF, window_only=True)
+    got = _check(c, f"out-of-window NaN pages {cd} window={window}")
     assert np.all(np.isfinite(got))
 
 
@@ -202,10 +219,13 @@ def test_hybrid_layers(variant):
     _check(c, f"hybrid {variant}")
 
 
-def test_hd256_long_decode():
-    # 8 q / 1 KV head, head_dim 256, 128k context
-    c = DecodeCase(1, 8, 1, 256, [131072], "e4m3", seed=5)
-    _check(c, "hd256 ctx=131072")
+@pytest.mark.parametrize("ctx", [1024, 8192, 32768, 131072])
+def test_hd256_long_decode(ctx):
+    # 8 q / 1 KV head, head_dim 256, per-head absmax scales, contexts to 128k
+    c = DecodeCase(1, 8, 1, 256, [ctx], "e4m3", seed=5)
+    _check(c, f"hd256 ctx={ctx}",
+           meta=dict(kernel="decode", shape="8/1 hd256 batch 1", context=ctx, cache="e4m3",
+                     compared="all heads"))
 
 
 def test_argument_errors_raise():
