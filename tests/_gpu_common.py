@@ -72,9 +72,12 @@ def assert_gate(gpu, ref, what, max_abs=MAX_ABS, rel_l2=REL_L2, slack=None, meta
     excess = diff if slack is None else np.maximum(diff - slack, 0.0)
     me = float(excess.max()) if excess.size else 0.0
     wr, wi = worst_row(gpu, ref)
+    nref = float(np.linalg.norm(np.asarray(ref, np.float64)))
+    rel_excess = float(np.linalg.norm(excess) / nref) if nref > 0 else float(np.linalg.norm(excess))
     extra = "" if slack is None else f" beyond-flip-allowance={me:.3e} (max allowance {float(np.max(slack)):.3e})"
     log(f"  {what}: max_abs={ma:.3e} rel_l2={rl:.3e} worst_row_rel_l2={wr:.3e}{extra}")
-    rec = dict(what=what, max_abs=ma, rel_l2=rl, excess=me, worst_row_rel_l2=wr,
+    rec = dict(what=what, max_abs=ma, rel_l2=rl, excess=me, rel_l2_excess=rel_excess,
+               worst_row_rel_l2=wr,
                worst_row=list(wi), elements=int(diff.size),
                finite=bool(np.all(np.isfinite(gpu))),
                passed=bool(me <= max_abs and rl <= rel_l2 and np.all(np.isfinite(gpu))))
