@@ -9,7 +9,7 @@ call raises ``RuntimeError`` (there is no fallback path).
 
 Names follow the C ABI in include/fa8attn.h:
     cache_write, absmax_scales, decode_num_splits, decode_workspace_bytes,
-    decode_attention, decode_attention_append, prefill_kv_tile,
+    decode_attention, decode_attention_noalloc, decode_attention_append, prefill_kv_tile,
     prefill_attention, stream_read, stream_copy
 """
 
@@ -19,8 +19,8 @@ import os
 __all__ = [
     "FA8_F32", "FA8_BF16", "FA8_E4M3", "FA8_E5M2", "BLOCK_SIZE", "Fa8Error", "library_path",
     "load", "cache_write", "absmax_scales", "decode_num_splits", "decode_workspace_bytes",
-    "decode_attention", "decode_attention_append", "prefill_kv_tile", "prefill_attention",
-    "new_cache",
+    "decode_attention", "decode_attention_noalloc", "decode_attention_append",
+    "prefill_kv_tile", "prefill_attention", "new_cache",
     "new_decode_workspace",
 ]
 
@@ -53,6 +53,9 @@ _SIGNATURES = {
     "fa8_decode_attention": (_I32, [_VP, _I32, _I32, _VP, _I32, _I64, _I32, _I32, _VP,
                                     _I32, _VP, _I32, _VP, _VP, _F32, _I32, _I32, _VP,
                                     _VP, _SZ, _VP]),
+    "fa8_decode_attention_noalloc": (_I32, [_VP, _I32, _I32, _VP, _I32, _I64, _I32, _I32, _VP,
+                                            _I32, _VP, _I32, _VP, _VP, _F32, _I32, _I32, _VP,
+                                            _VP]),
     "fa8_decode_attention_append": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _VP, _I32, _I64,
                                             _I32, _I32, _VP, _I32, _VP, _I32, _VP, _VP, _F32,
                                             _I32, _I32, _VP, _VP, _SZ, _VP]),
@@ -248,6 +251,9 @@ def new_decode_workspace(nbytes, device="cuda"):
     return torch.zeros(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
 
+_NO_WORKSPACE = object()   # the allocation-free entry point takes none
+
+
 def _decode_args(q, cache, block_table, seq_lens, k_scale, v_scale, max_seq_len, window,
                  num_splits, out, workspace):
     torch = _torch()
@@ -267,9 +273,10 @@ def _decode_args(q, cache, block_table, seq_lens, k_scale, v_scale, max_seq_len,
         _require(k_scale, "k_scale", dtype=torch.float32, device=dev, ndim=1)
         _require(v_scale, "v_scale", dtype=torch.float32, device=dev, ndim=1)
     splits = num_splits or decode_num_splits(B, hkv, int(max_seq_len), int(window))
-    need = decode_workspace_bytes(B, hq, d, splits)
-    if workspace is None:
-        workspace = new_decode_workspace(need, dev)
+    if workspace is _NO_WORKSPACE:
+        workspace = None
+    elif workspace is None:
+        workspace = new_decode_workspace(decode_workspace_bytes(B, hq, d, splits), dev)
     else:
         _require(workspace, "workspace", device=dev)
     if out is None:
@@ -299,6 +306,22 @@ def decode_attention(q, cache, block_table, seq_lens, k_scale, v_scale, sm_scale
     _check(lib.fa8_decode_attention(
         *head, *tail, float(sm_scale), int(window), int(splits), _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(cache)))
+    return out
+
+
+def decode_attention_noalloc(q, cache, block_table, seq_lens, k_scale, v_scale, sm_scale,
+                             max_seq_len, out, window=0, num_splits=0):
+    """decode_attention without a workspace: the library's fixed per-GPU
+    scratch holds the split partials, so the call allocates nothing (``out``
+    is required).  Calls that overlap on one GPU share that scratch and must
+    be ordered on one stream."""
+    lib = load()
+    _require(out, "out")
+    head, tail, splits, out, _ = _decode_args(
+        q, cache, block_table, seq_lens, k_scale, v_scale, max_seq_len, window, num_splits,
+        out, _NO_WORKSPACE)
+    _check(lib.fa8_decode_attention_noalloc(
+        *head, *tail, float(sm_scale), int(window), int(splits), _ptr(out), _stream(cache)))
     return out
 
 

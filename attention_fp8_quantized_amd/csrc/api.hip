@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/fa8attn.h"
@@ -73,6 +74,68 @@ int decode_pages_max(int max_seq_len, int window) {
   const int visible = window > 0 ? std::min(window, max_seq_len) : max_seq_len;
   // a window that does not start on a page boundary spans one extra page
   return (visible + FA8_BLOCK_SIZE - 1) / FA8_BLOCK_SIZE + (window > 0 ? 1 : 0);
+}
+
+}  // namespace
+
+// ---- scratch of the allocation-free decode entry point ----------------------
+// Split partials and arrival counters of fa8_decode_attention_noalloc live in
+// this array instead of a caller's workspace: the first
+// FA8_DECODE_SCRATCH_COUNTERS int32 are the arrival counters (zero between
+// calls: cleared once per device, then re-armed by every call), the rest
+// holds the partials.  Each GPU the library runs on has its own copy, held
+// until the process ends.  Host code never uses the name itself (it is a
+// host-side stand-in, not a device address): kernels and fills get the
+// per-device address hipGetSymbolAddress returns.
+static __device__ __align__(256) unsigned char scratch[FA8_DECODE_SCRATCH_BYTES];
+
+namespace {
+
+constexpr size_t kScratchCounterBytes = (size_t)FA8_DECODE_SCRATCH_COUNTERS * 4;
+constexpr int kMaxDevices = 64;
+
+struct ScratchSlot {
+  void* ptr = nullptr;   // device address of `scratch` on this device
+  bool cleared = false;  // counters cleared by a call that ran eagerly
+};
+ScratchSlot g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+__global__ void zero_words_kernel(uint32_t* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// Device address of this device's scratch; on a call that is not being
+// captured into a graph and finds the counters not yet cleared, the counter
+// region is cleared first on `stream` (a kernel, not a memset, so that a
+// captured call records an ordinary kernel node; a captured call clears on
+// every replay until an eager call has cleared them).
+fa8_status scratch_for_call(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "decode_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(FA8_EUNSUPPORTED, "decode_noalloc: device ordinal %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchSlot& slot = g_scratch[dev];
+  if (!slot.ptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return hip_fail(e, "decode_noalloc: hipGetSymbolAddress");
+    slot.ptr = ptr;
+  }
+  if (!slot.cleared) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(stream, &cap);
+    if (e != hipSuccess) return hip_fail(e, "decode_noalloc: hipStreamIsCapturing");
+    hipLaunchKernelGGL(zero_words_kernel, dim3(16), dim3(256), 0, stream,
+                       reinterpret_cast<uint32_t*>(slot.ptr), FA8_DECODE_SCRATCH_COUNTERS);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "decode_noalloc: counter clear launch");
+    if (cap == hipStreamCaptureStatusNone) slot.cleared = true;
+  }
+  *out = slot.ptr;
+  return FA8_OK;
 }
 
 }  // namespace
@@ -177,7 +240,8 @@ static fa8_status decode_impl(const void* q, int32_t batch, int32_t num_q_heads,
                               const float* k_scale, const float* v_scale, float sm_scale,
                               int32_t window, int32_t num_splits, float* out,
                               void* workspace, size_t workspace_bytes, void* stream,
-                              const void* k_new, const void* v_new, int32_t new_dtype) {
+                              const void* k_new, const void* v_new, int32_t new_dtype,
+                              bool use_scratch = false) {
   if (batch < 0) return fail(FA8_EINVAL, "decode: batch < 0");
   if (num_q_heads <= 0 || num_kv_heads <= 0)
     return fail(FA8_EINVAL, "decode: head counts must be > 0");
@@ -202,28 +266,45 @@ static fa8_status decode_impl(const void* q, int32_t batch, int32_t num_q_heads,
   if (batch > kMaxGridYZ || num_kv_heads > kMaxGridYZ)
     return fail(FA8_EUNSUPPORTED, "decode: batch and num_kv_heads must be <= %d", kMaxGridYZ);
   if (batch == 0) return ok();
-  if (!q || !cache || !block_table || !seq_lens || !out || !workspace)
+  if (!q || !cache || !block_table || !seq_lens || !out || (!use_scratch && !workspace))
     return fail(FA8_EINVAL, "decode: null pointer argument");
   if (fp8_cache(cache_dtype) && (!k_scale || !v_scale))
     return fail(FA8_EINVAL, "decode: an FP8 cache needs k_scale and v_scale");
-  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+  if (!use_scratch && reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
     return fail(FA8_EINVAL, "decode: workspace must be 16-byte aligned");
 
   const int S = num_splits > 0 ? num_splits
                                : fa8_decode_num_splits(batch, num_kv_heads, max_seq_len, window);
-  const size_t need = fa8::decode_workspace_bytes(batch, num_q_heads, head_dim, S);
-  if (workspace_bytes < need)
-    return fail(FA8_EINVAL, "decode: workspace has %zu bytes, %zu needed for %d splits",
-                workspace_bytes, need, S);
-
   fa8::DecodeParams p{};
+  if (use_scratch) {
+    const size_t cb = fa8::decode_counter_bytes(batch, num_q_heads, S);
+    const size_t pb = fa8::decode_partial_bytes(batch, num_q_heads, head_dim, S);
+    if (cb > kScratchCounterBytes || pb > FA8_DECODE_SCRATCH_BYTES - kScratchCounterBytes)
+      return fail(FA8_EINVAL,
+                  "decode_noalloc: %d splits need %zu counter bytes and %zu partial bytes; "
+                  "the scratch holds at most %zu and %zu",
+                  S, cb, pb, kScratchCounterBytes,
+                  (size_t)FA8_DECODE_SCRATCH_BYTES - kScratchCounterBytes);
+    void* base = nullptr;
+    const fa8_status st = scratch_for_call(reinterpret_cast<hipStream_t>(stream), &base);
+    if (st != FA8_OK) return st;
+    fa8::decode_workspace_carve_split(reinterpret_cast<int*>(base),
+                                      reinterpret_cast<char*>(base) + kScratchCounterBytes,
+                                      batch, num_q_heads, head_dim, S, p);
+  } else {
+    const size_t need = fa8::decode_workspace_bytes(batch, num_q_heads, head_dim, S);
+    if (workspace_bytes < need)
+      return fail(FA8_EINVAL, "decode: workspace has %zu bytes, %zu needed for %d splits",
+                  workspace_bytes, need, S);
+    fa8::decode_workspace_carve(workspace, batch, num_q_heads, head_dim, S, p);
+  }
+
   p.q = reinterpret_cast<const uint16_t*>(q);
   p.cache = reinterpret_cast<const uint8_t*>(cache);
   p.block_table = block_table;
   p.seq_lens = seq_lens;
   p.k_scale = k_scale;
   p.v_scale = v_scale;
-  fa8::decode_workspace_carve(workspace, batch, num_q_heads, head_dim, S, p);
   p.out = out;
   p.batch = batch;
   p.num_q_heads = num_q_heads;
@@ -259,6 +340,20 @@ fa8_status fa8_decode_attention(const void* q, int32_t batch, int32_t num_q_head
                      head_dim, block_table, max_blocks_per_seq, seq_lens, max_seq_len, k_scale,
                      v_scale, sm_scale, window, num_splits, out, workspace, workspace_bytes,
                      stream, nullptr, nullptr, FA8_F32);
+}
+
+fa8_status fa8_decode_attention_noalloc(const void* q, int32_t batch, int32_t num_q_heads,
+                                        const void* cache, int32_t cache_dtype,
+                                        int64_t num_blocks, int32_t num_kv_heads,
+                                        int32_t head_dim, const int32_t* block_table,
+                                        int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                        int32_t max_seq_len, const float* k_scale,
+                                        const float* v_scale, float sm_scale, int32_t window,
+                                        int32_t num_splits, float* out, void* stream) {
+  return decode_impl(q, batch, num_q_heads, cache, cache_dtype, num_blocks, num_kv_heads,
+                     head_dim, block_table, max_blocks_per_seq, seq_lens, max_seq_len, k_scale,
+                     v_scale, sm_scale, window, num_splits, out, nullptr, 0, stream, nullptr,
+                     nullptr, FA8_F32, true);
 }
 
 fa8_status fa8_decode_attention_append(const void* q, const void* k_new, const void* v_new,

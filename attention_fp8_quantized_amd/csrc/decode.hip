@@ -717,23 +717,31 @@ static size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
 // Counter sets are bounded by B * Hq (one per sequence, KV head and head
 // group).
-size_t decode_workspace_bytes(int batch, int num_q_heads, int head_dim, int splits) {
+size_t decode_counter_bytes(int batch, int num_q_heads, int splits) {
+  const size_t heads = (size_t)batch * num_q_heads;
+  return align16(heads * (decode_num_groups(splits) + 1) * 4);
+}
+
+size_t decode_partial_bytes(int batch, int num_q_heads, int head_dim, int splits) {
   const size_t heads = (size_t)batch * num_q_heads;
   const int ng = decode_num_groups(splits);
-  size_t n = align16(heads * (ng + 1) * 4);
-  n += align16(heads * splits * head_dim * 4) + 2 * align16(heads * splits * 4);
+  size_t n = align16(heads * splits * head_dim * 4) + 2 * align16(heads * splits * 4);
   if (ng > 1) n += align16(heads * ng * head_dim * 4) + 2 * align16(heads * ng * 4);
   return n;
 }
 
-void decode_workspace_carve(void* ws, int batch, int num_q_heads, int head_dim, int splits,
-                            DecodeParams& p) {
+size_t decode_workspace_bytes(int batch, int num_q_heads, int head_dim, int splits) {
+  return decode_counter_bytes(batch, num_q_heads, splits) +
+         decode_partial_bytes(batch, num_q_heads, head_dim, splits);
+}
+
+void decode_workspace_carve_split(int* counters, void* partials, int batch, int num_q_heads,
+                                  int head_dim, int splits, DecodeParams& p) {
   const size_t heads = (size_t)batch * num_q_heads;
   const int ng = decode_num_groups(splits);
-  char* at = reinterpret_cast<char*>(ws);
-  p.ws_count = reinterpret_cast<int*>(at);
-  p.ws_count2 = p.ws_count + heads * ng;
-  at += align16(heads * (ng + 1) * 4);
+  p.ws_count = counters;
+  p.ws_count2 = counters + heads * ng;
+  char* at = reinterpret_cast<char*>(partials);
   p.ws_o = reinterpret_cast<float*>(at);
   at += align16(heads * splits * head_dim * 4);
   p.ws_m = reinterpret_cast<float*>(at);
@@ -748,6 +756,14 @@ void decode_workspace_carve(void* ws, int batch, int num_q_heads, int head_dim, 
     at += align16(heads * ng * 4);
     p.ws_l1 = reinterpret_cast<float*>(at);
   }
+}
+
+void decode_workspace_carve(void* ws, int batch, int num_q_heads, int head_dim, int splits,
+                            DecodeParams& p) {
+  decode_workspace_carve_split(reinterpret_cast<int*>(ws),
+                               reinterpret_cast<char*>(ws) +
+                                   decode_counter_bytes(batch, num_q_heads, splits),
+                               batch, num_q_heads, head_dim, splits, p);
 }
 
 #ifndef FA8_DECODE_PIPE

@@ -73,6 +73,12 @@ constexpr int kDecodeWaves = FA8_DECODE_WAVES;   // waves per decode workgroup
 size_t decode_workspace_bytes(int batch, int num_q_heads, int head_dim, int splits);
 void decode_workspace_carve(void* ws, int batch, int num_q_heads, int head_dim, int splits,
                             DecodeParams& p);
+// The same layout in two pieces: the counters (decode_counter_bytes, zero
+// between calls) and the partials (decode_partial_bytes, no initial value).
+size_t decode_counter_bytes(int batch, int num_q_heads, int splits);
+size_t decode_partial_bytes(int batch, int num_q_heads, int head_dim, int splits);
+void decode_workspace_carve_split(int* counters, void* partials, int batch, int num_q_heads,
+                                  int head_dim, int splits, DecodeParams& p);
 
 // fmt: kFmtE4m3, kFmtE5m2 or kFmtBf16 (fa8_device.hpp)
 hipError_t launch_decode(const DecodeParams& p, int fmt, hipStream_t stream);

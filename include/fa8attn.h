@@ -191,6 +191,44 @@ fa8_status fa8_decode_attention(const void* q, int32_t batch,
                                 void* stream);
 
 /*
+ * Allocation-free decode, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same operation, arguments, results and errors as
+ * fa8_decode_attention, without the workspace: the split partials and
+ * arrival counters live in a fixed scratch array inside the library,
+ * FA8_DECODE_SCRATCH_BYTES on each GPU the library runs on, held until the
+ * process ends.  The call allocates nothing (no hipMalloc, no allocating
+ * library routine).
+ * Limits (FA8_EINVAL beyond them, before anything is launched), with S the
+ * split count (num_splits, or fa8_decode_num_splits(...) when 0):
+ *   batch * num_q_heads * (NG + 1) <= FA8_DECODE_SCRATCH_COUNTERS, where
+ *     NG = 1 for S <= 64, else ceil(S / 16), and
+ *   fa8_decode_workspace_bytes(batch, num_q_heads, head_dim, S) minus the
+ *     counters' 16-byte-aligned bytes <= FA8_DECODE_SCRATCH_BYTES - 4 *
+ *     FA8_DECODE_SCRATCH_COUNTERS
+ *   (e.g. 32 query heads, head_dim 128, batch 8 and up to 100 splits fit).
+ * Every call on a GPU shares that GPU's scratch, which keeps the last call's
+ * partials: calls that overlap on one GPU (two streams, two threads without
+ * ordering) race and give wrong results, so order them on one stream.  The
+ * counters must be zero at the start of a call; every call leaves them
+ * zero, and the first call on a device that is not being captured clears
+ * them first with a small kernel on `stream` (a captured call records that
+ * clear in its graph until an eager call has done it).
+ */
+#define FA8_DECODE_SCRATCH_BYTES (16u << 20)
+#define FA8_DECODE_SCRATCH_COUNTERS 16384
+fa8_status fa8_decode_attention_noalloc(const void* q, int32_t batch,
+                                        int32_t num_q_heads, const void* cache,
+                                        int32_t cache_dtype, int64_t num_blocks,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        const int32_t* block_table,
+                                        int32_t max_blocks_per_seq,
+                                        const int32_t* seq_lens, int32_t max_seq_len,
+                                        const float* k_scale, const float* v_scale,
+                                        float sm_scale, int32_t window,
+                                        int32_t num_splits, float* out, void* stream);
+
+/*
  * Fused decode step: write the current token's K/V into the cache and attend
  * over the context including it, in one launch.  [BLOG] "Kernel 与 vLLM 改进"
  * and "单请求 Benchmark": quantising the new token is a fixed per-step cost

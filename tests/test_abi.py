@@ -158,6 +158,39 @@ def test_decode_rejects_bad_arguments(lib):
     assert _decode(lib, B=0) == 0                            # empty batch: no-op
 
 
+def _decode_noalloc(lib, **over):
+    fake = _p(0x1000)
+    a = dict(q=fake, B=1, Hq=8, cache=fake, cd=2, nb=4, Hkv=2, D=64, bt=fake, mb=4,
+             lens=fake, maxlen=64, ks=fake, vs=fake, sm=0.125, window=0, splits=1,
+             out=fake, stream=None)
+    a.update(over)
+    return lib.fa8_decode_attention_noalloc(a["q"], a["B"], a["Hq"], a["cache"], a["cd"],
+                                            a["nb"], a["Hkv"], a["D"], a["bt"], a["mb"],
+                                            a["lens"], a["maxlen"], a["ks"], a["vs"], a["sm"],
+                                            a["window"], a["splits"], a["out"], a["stream"])
+
+
+@fake_pointers
+def test_decode_noalloc_rejects_bad_arguments_and_oversized_layouts(lib):
+    # the same checks as the workspace entry point ...
+    assert _decode_noalloc(lib, Hq=7) == EINVAL
+    assert _decode_noalloc(lib, D=96) == EUNSUPPORTED
+    assert _decode_noalloc(lib, q=None) == EINVAL
+    assert _decode_noalloc(lib, splits=257) == EINVAL
+    assert _decode_noalloc(lib, B=0) == 0                    # empty batch: no-op
+    # ... and layouts beyond the fixed scratch: 64 x 16 heads x 256 splits
+    # of 256 floats need 287 MB of partials (and 69,632 counter bytes)
+    assert _decode_noalloc(lib, B=64, Hq=16, Hkv=1, D=256, splits=256) == EINVAL
+    assert b"scratch" in lib.fa8_last_error()
+    # partials alone too large: 8 x 32 heads x 256 splits x 128 floats
+    # (33.6 MB), counters small
+    assert _decode_noalloc(lib, B=8, Hq=32, Hkv=8, D=128, splits=256) == EINVAL
+    assert b"scratch" in lib.fa8_last_error()
+    # counters alone too large: 16384 heads at one split (2 counters each)
+    assert _decode_noalloc(lib, B=1024, Hq=16, Hkv=16, D=64, splits=1) == EINVAL
+    assert b"counter" in lib.fa8_last_error()
+
+
 def _decode_append(lib, **over):
     fake = _p(0x1000)
     a = dict(q=fake, kn=fake, vn=fake, idt=0, B=1, Hq=8, cache=fake, cd=2, nb=4, Hkv=2, D=64,
