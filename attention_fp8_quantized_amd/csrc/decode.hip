@@ -27,9 +27,10 @@
 //     keys 4g..4g+3 for query head n;
 //   * softmax in the log2 domain: page maximum per head across the 4 lane
 //     groups (permlane swaps), lazily moved reference maximum, p = 2^(s - m);
-//   * P . V on v_mfma_f32_16x16x16 (f16 for the FP8 caches: p rounded to f16,
-//     V widened to f16 exactly; bf16 for the bf16 cache with p split into a
-//     bf16 high and low part, two products): lane (n, g) already holds P for
+//   * P . V on v_mfma_f32_16x16x16 (f16 for the FP8 caches: p split into an
+//     f16 high and low part, V widened to f16 exactly; bf16 for the bf16
+//     cache with p split into a bf16 high and low part; two products each):
+//     lane (n, g) already holds P for
 //     head n and keys 4g..4g+3, the A operand.  V is written to a small
 //     per-wave LDS slice and read back transposed (ds_read_b64_tr_b8 / _b16)
 //     as the B operand (keys 4g..4g+3 of one column per lane).  The output
@@ -43,6 +44,12 @@
 
 #include "fa8_device.hpp"
 #include "fa8_internal.hpp"
+
+// FP8 caches: P enters the P.V product as an f16 high and low part (1) or
+// as one f16 value (0).
+#ifndef FA8_DECODE_P_SPLIT
+#define FA8_DECODE_P_SPLIT 1
+#endif
 
 namespace fa8 {
 
@@ -517,7 +524,13 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFmt>())) void decode
     // ---- P . V ---------------------------------------------------------------
     // V slice hh: bytes [64 hh, 64 hh + 64) of the 16 rows, row-major in LDS
     if constexpr (kFp8) {
+      // p = hi + lo, both f16 (together 22 significant bits; V is exact in
+      // f16, so each product pair carries p to about 2^-22)
       const f16x4 pa = {(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
+#if FA8_DECODE_P_SPLIT
+      const f16x4 pl = {(_Float16)(pr[0] - (float)pa[0]), (_Float16)(pr[1] - (float)pa[1]),
+                        (_Float16)(pr[2] - (float)pa[2]), (_Float16)(pr[3] - (float)pa[3])};
+#endif
 #pragma unroll
       for (int hh = 0; hh < NL; ++hh) {
         *reinterpret_cast<uint4*>(sv + n * RS + 16 * g) = pg.v[hh];
@@ -533,7 +546,12 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFmt>())) void decode
           const f16x2 v01 = fp8x2_to_f16<kFmt, false>(codes);
           const f16x2 v23 = fp8x2_to_f16<kFmt, true>(codes);
           const f16x4 vb = {v01[0], v01[1], v23[0], v23[1]};
-          o[hh * BPS + cb] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vb, o[hh * BPS + cb], 0, 0, 0);
+          f32x4 acc = o[hh * BPS + cb];
+          acc = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vb, acc, 0, 0, 0);
+#if FA8_DECODE_P_SPLIT
+          acc = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, vb, acc, 0, 0, 0);
+#endif
+          o[hh * BPS + cb] = acc;
         }
       }
     } else {

@@ -748,7 +748,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e4m3 cache, f32 math",
+        "dtype": "e4m3 cache; QK on bf16 products (exact e4m3 widening), P.V on f16 "
+                 "products with P as an f16 high+low pair, fp32 accumulation",
         "data": "synthetic: N(0,1) K/V with 1% outlier channels x20, absmax/448 per-KV-head "
                 "scales, device RNG",
         "step": {"kernels": "decode_attention_append per layer (the current token's cache "
