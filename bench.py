@@ -748,8 +748,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e4m3 cache; QK on bf16 products (exact e4m3 widening), P.V on f16 "
-                 "products with P as an f16 high+low pair, fp32 accumulation",
+        "dtype": "e4m3 KV cache; bf16 QK, f16 hi+lo P.V, f32 accumulate",
         "data": "synthetic: N(0,1) K/V with 1% outlier channels x20, absmax/448 per-KV-head "
                 "scales, device RNG",
         "step": {"kernels": "decode_attention_append per layer (the current token's cache "
