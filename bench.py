@@ -591,9 +591,21 @@ def measure_cache_write_bulk(fa, torch, reps=10):
     return res
 
 
-def cpu_baseline(Hq, Hkv, D, ctx, budget_s=10.0):
-    """The fp64 oracle decoding one Llama-shaped layer at ``ctx`` on the host
-    (bounded sample: one layer, repeated until ``budget_s`` of CPU time)."""
+def cpu_baseline(Hq, Hkv, D, ctx, reps=2):
+    """The fp64 NumPy oracle timed on the host cores (bounded samples of the
+    same workloads; about 15-30 s of CPU work):
+
+    * decode_attention on one Llama-shaped layer at the contexts 1k, 8k,
+      32k and 128k (best of ``reps``), with the linear fit
+      ms = slope * context + intercept (the pages' ITL-slope form); the 128k
+      cache is the 32k layer's codes repeated four times (distinct memory, the
+      same work per token);
+    * quantize_rows (the cache-write encoding) on 4096 tokens of K: tokens/s;
+    * prefill_mirror on the head_dim-256 32k chunk (8 query / 1 KV head):
+      seconds per query row at the end of the chunk (32k visible keys, all 8
+      heads), extrapolated to the whole causal chunk (rows see (i+1) keys, so
+      the chunk costs about T/2 such rows).
+    ``value`` is the 32k decode rate in GB/s of algorithmic bytes."""
     import workloads as W
     from oracle import attention as OA
     from oracle import quant as OQ
@@ -602,33 +614,76 @@ def cpu_baseline(Hq, Hkv, D, ctx, budget_s=10.0):
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         blas_threads = 1
+    cores = len(os.sched_getaffinity(0))
+    t_start = time.perf_counter()
     lens = np.array([ctx], np.int32)
     bt, nb = W.block_table(W.rng(2, 0, W.BLOCKS), lens)
     k = W.with_outliers(W.normal(W.rng(2, 0, W.K), (ctx, Hkv, D)), W.rng(2, 0, W.OUTLIERS))
     v = W.with_outliers(W.normal(W.rng(2, 0, W.V), (ctx, Hkv, D)), W.rng(2, 1, W.OUTLIERS))
     ks, vs = W.absmax_scales(k), W.absmax_scales(v)
+    # quantize_rows: the cache write's encoding of 4096 K rows
+    t0 = time.perf_counter()
+    OQ.quantize_rows(k[:4096], ks[None, :, None])
+    quant_tps = 4096 / (time.perf_counter() - t0)
     cache = OQ.cache_write(OQ.new_cache(nb, Hkv, D, "e4m3"), k, v, W.all_slots(bt, lens),
                            ks, vs, "e4m3")
     del k, v
     _, q = W.bf16_values(W.normal(W.rng(2, 0, W.Q), (1, Hq, D)))
     sm = np.float32(1 / math.sqrt(D))
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        OA.decode_attention(q, cache, bt, lens, ks, vs, sm, 0, "e4m3", Hkv)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    per_layer = el / n
-    gbs = decode_bytes(1, Hq, Hkv, D, ctx, 1) / per_layer / 1e9
-    cores = len(os.sched_getaffinity(0))
+    # 128k: four copies of the 32k layer's pages
+    rep = 131072 // ctx
+    cache4 = np.concatenate([cache] * rep, axis=0)
+    bt4 = np.concatenate([bt[:, :ctx // 16] + r * nb for r in range(rep)], axis=1)
+    decode_ms = {}
+    for c in (1024, 8192, 32768, 131072):
+        cc, bb = (cache, bt) if c <= ctx else (cache4, bt4)
+        best = float("inf")
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            OA.decode_attention(q, cc, bb, np.array([c], np.int32), ks, vs, sm, 0, "e4m3", Hkv)
+            best = min(best, time.perf_counter() - t0)
+        decode_ms[c] = best * 1e3
+    del cache4
+    ctxs = sorted(decode_ms)
+    slope, icpt = np.polyfit(np.array(ctxs, float), np.array([decode_ms[c] for c in ctxs]), 1)
+    gbs = decode_bytes(1, Hq, Hkv, D, ctx, 1) / (decode_ms[ctx] * 1e-3) / 1e9
+    # prefill mirror: the last rows of the head_dim-256 32k chunk
+    T, Hq5, Hkv5, D5 = 32768, 8, 1, 256
+    lens5 = np.array([T], np.int32)
+    bt5, nb5 = W.block_table(W.rng(5, 0, W.BLOCKS), lens5)
+    k5 = W.normal(W.rng(5, 0, W.K), (T, Hkv5, D5))
+    v5 = W.normal(W.rng(5, 0, W.V), (T, Hkv5, D5))
+    ks5, vs5 = W.absmax_scales(k5), W.absmax_scales(v5)
+    cache5 = OQ.cache_write(OQ.new_cache(nb5, Hkv5, D5, "e4m3"), k5, v5,
+                            W.all_slots(bt5, lens5), ks5, vs5, "e4m3")
+    del k5, v5
+    rows = np.arange(T - 4, T)
+    q5 = np.zeros((T, Hq5, D5), np.float32)
+    q5[rows] = W.bf16_values(W.normal(W.rng(5, 0, W.Q), (len(rows), Hq5, D5)))[1]
+    qs5 = np.float32(np.abs(q5[rows]).max() / 448.0)
+    cu5 = np.array([0, T], np.int32)
+    times = {}
+    for n in (1, len(rows)):
+        t0 = time.perf_counter()
+        OA.prefill_mirror(q5, cu5, cache5, bt5, lens5, qs5, ks5, vs5, np.float32(1 / 16.0), 0,
+                          128, rows=rows[-n:])
+        times[n] = time.perf_counter() - t0
+    per_row = (times[len(rows)] - times[1]) / (len(rows) - 1)
+    total_s = time.perf_counter() - t_start
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": min(cores, max(blas_threads, 1)),
             "kind": "oracle",
-            "sample": f"{n} decode call(s) of one {ctx}-token Llama-shaped layer "
-                      f"(32/8 heads, hd128, fp8 cache), fp64 NumPy, "
-                      f"{per_layer * 1e3:.1f} ms per layer; host cores available {cores}, "
-                      f"BLAS threads {blas_threads}"}
+            "sample": f"unoptimized fp64 NumPy reference on {cores} host cores "
+                      f"({blas_threads} BLAS threads): decode of one Llama-shaped layer "
+                      f"(32/8 heads, hd128, e4m3 cache) at 1k/8k/32k/128k, best of {reps}; "
+                      f"quantize_rows on 4096 tokens; prefill_mirror on the last 4 rows of "
+                      f"the hd256 32k chunk; {total_s:.1f} s in all",
+            "host_cores": cores, "blas_threads": blas_threads,
+            "decode_ms": {str(c): round(decode_ms[c], 3) for c in ctxs},
+            "decode_slope_ms_per_ctx_token": float(f"{slope:.4g}"),
+            "decode_intercept_ms": round(float(icpt), 3),
+            "quantize_rows_tokens_per_s": round(quant_tps, 1),
+            "prefill_mirror_s_per_row_at_32k": round(per_row, 4),
+            "prefill_32k_chunk_extrapolated_s": round(per_row * T / 2, 1)}
 
 
 def copy_calibration(fa, torch, nbytes=256 << 20, reps=4):
