@@ -115,6 +115,9 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 // s_waitcnt immediate: wait until at most n vector-memory operations are
 // outstanding (lgkm and exp counters not waited on); n up to 63
 constexpr int vmcnt_imm(int n) { return 0x3F70 | (n & 15) | ((n >> 4) << 14); }
+// s_waitcnt immediate: wait until every LDS operation of this wave is done
+// (vector-memory and exp counters not waited on)
+constexpr int kLgkm0 = 0xC07F;
 
 // MB = query blocks of 16 rows per wave; the workgroup has 8/MB waves and
 // always 128 query rows.  With MB = 2 each widened K operand and each V^T
@@ -240,13 +243,14 @@ __global__ __launch_bounds__(64 * (8 / MB)) void prefill_kernel(PrefillParams p)
   };
 
   // Block id of page `page` of the sequence.  Only the entries of pages
-  // pg_lo .. n_pages-1 are ever read: pg_lo holds the first key any row of
-  // this block can see, so entries outside the window (a freed page, -1) are
-  // never dereferenced.  A staged tile that reaches below pg_lo or past the
-  // end copies the nearest visible page instead; those rows are masked in
-  // the scores and their V rows zeroed after the copy.
-  const int pg_lo = lo_key / kBlockSize;
-  auto page_blk = [&](int page) { return bt[min(max(page, pg_lo), n_pages - 1)]; };
+  // lo_key/16 .. n_pages-1 are ever read (lo_key is the first key any row of
+  // this block can see), so entries outside the window (a freed page, -1)
+  // are never dereferenced.  A staged tile that reaches below the window or
+  // past the end copies the nearest visible page instead; those rows are
+  // masked in the scores and their V rows zeroed after the copy.  Inside the
+  // tile loop the pages fetched (tile t+2 >= t_lo+2) all lie above the
+  // window start, so only the end needs the clamp there.
+  auto page_blk = [&](int page) { return bt[page < n_pages ? page : n_pages - 1]; };
   // Copy u of this wave (0..NCOPY-1) fills rows row0 .. row0+RPI-1 of the K
   // (first TILE bytes) or V tile, one 16-byte chunk per lane.  The row of a
   // lane within its page, and so its swizzle, depends on u at most through
@@ -277,13 +281,30 @@ __global__ __launch_bounds__(64 * (8 / MB)) void prefill_kernel(PrefillParams p)
     }
   };
 
-  // block ids of the first two tiles
+  // block ids of the first two tiles (pages below the window start read the
+  // first visible page's entry instead)
   if (threadIdx.x < 2 * PPT) {
     const int t = t_lo + threadIdx.x / PPT;
-    s_bt[t & 3][threadIdx.x % PPT] = page_blk(t * PPT + threadIdx.x % PPT);
+    s_bt[t & 3][threadIdx.x % PPT] = page_blk(max(t * PPT + threadIdx.x % PPT, lo_key / kBlockSize));
   }
   __syncthreads();
   stage(s_buf0, t_lo & 3);
+  // A window that starts inside the first tile: its V rows before the first
+  // visible key hold another page's rows or a stale page's bytes (NaN codes,
+  // say), and P = 0 times NaN would be NaN.  Wait for this tile's copies and
+  // zero those rows; the first tile's barrier publishes them.
+  if (lo_key > t_lo * kTileN) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    const int rows_lo = lo_key - t_lo * kTileN;
+#pragma unroll
+    for (int u = 0; u < NCOPY; ++u) {
+      const int idx = u * NWV + wave;
+      const int row0 = (idx % CPT) * RPI;
+      if (idx / CPT == 1 && row0 + lane / (D / 16) < rows_lo)
+        *reinterpret_cast<uint4*>(s_buf0 + TILE + row0 * D + lane * 16) = make_uint4(0, 0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(kLgkm0);
+  }
 
   // One tile.  kOdd selects the buffer roles at compile time (the tile loop is
   // unrolled by two), so the compiler sees that the copies in flight target
@@ -303,22 +324,21 @@ __global__ __launch_bounds__(64 * (8 / MB)) void prefill_kernel(PrefillParams p)
     // but the id load and the NCOPY copies just issued
     stage(nxt, (t + 1) & 3);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(NCOPY + 1));
-    // V rows no row of this block can see: past the sequence end (the tail
-    // tile) or before the first visible key (the first tile of a windowed
-    // block).  They hold another page's rows or whatever a stale page held,
-    // and P = 0 times NaN would be NaN, so every lane overwrites the V chunks
-    // it copied there with zeros before the barrier publishes them.
-    if ((t + 1) * kTileN > L || t * kTileN < lo_key) {
-      const int rows_lo = lo_key - t * kTileN;
-      const int rows_hi = L - t * kTileN;
+    // rows past the sequence end (the tail tile only): they hold another
+    // page's rows or whatever a stale page held, and P = 0 times NaN would
+    // be NaN, so every lane overwrites the V chunks it copied there with
+    // zeros before the barrier publishes them (rows before a window start:
+    // the prologue)
+    if ((t + 1) * kTileN > L) {
+      const int rows_left = L - t * kTileN;
 #pragma unroll
       for (int u = 0; u < NCOPY; ++u) {
         const int idx = u * NWV + wave;
-        const int r = (idx % CPT) * RPI + lane / (D / 16);
-        if (idx / CPT == 1 && (r < rows_lo || r >= rows_hi))
-          *reinterpret_cast<uint4*>(cur + TILE + (r - lane / (D / 16)) * D + lane * 16) =
-              make_uint4(0, 0, 0, 0);
+        const int row0 = (idx % CPT) * RPI;
+        if (idx / CPT == 1 && row0 + lane / (D / 16) >= rows_left)
+          *reinterpret_cast<uint4*>(cur + TILE + row0 * D + lane * 16) = make_uint4(0, 0, 0, 0);
       }
+      __builtin_amdgcn_s_waitcnt(kLgkm0);   // the zeros land before the barrier
     }
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);

@@ -591,7 +591,7 @@ def measure_cache_write_bulk(fa, torch, reps=10):
     return res
 
 
-def cpu_baseline(Hq, Hkv, D, ctx, reps=2):
+def cpu_baseline(Hq, Hkv, D, ctx, reps=5, prefill_rows=16):
     """The fp64 NumPy oracle timed on the host cores (bounded samples of the
     same workloads; about 15-30 s of CPU work):
 
@@ -602,9 +602,10 @@ def cpu_baseline(Hq, Hkv, D, ctx, reps=2):
       same work per token);
     * quantize_rows (the cache-write encoding) on 4096 tokens of K: tokens/s;
     * prefill_mirror on the head_dim-256 32k chunk (8 query / 1 KV head):
-      seconds per query row at the end of the chunk (32k visible keys, all 8
-      heads), extrapolated to the whole causal chunk (rows see (i+1) keys, so
-      the chunk costs about T/2 such rows).
+      seconds per query row at the end of the chunk (the last
+      ``prefill_rows`` rows, 32k visible keys, all 8 heads), extrapolated to
+      the whole causal chunk (rows see (i+1) keys, so the chunk costs about
+      T/2 such rows).
     ``value`` is the 32k decode rate in GB/s of algorithmic bytes."""
     import workloads as W
     from oracle import attention as OA
@@ -657,7 +658,7 @@ def cpu_baseline(Hq, Hkv, D, ctx, reps=2):
     cache5 = OQ.cache_write(OQ.new_cache(nb5, Hkv5, D5, "e4m3"), k5, v5,
                             W.all_slots(bt5, lens5), ks5, vs5, "e4m3")
     del k5, v5
-    rows = np.arange(T - 4, T)
+    rows = np.arange(T - prefill_rows, T)
     q5 = np.zeros((T, Hq5, D5), np.float32)
     q5[rows] = W.bf16_values(W.normal(W.rng(5, 0, W.Q), (len(rows), Hq5, D5)))[1]
     qs5 = np.float32(np.abs(q5[rows]).max() / 448.0)
@@ -675,7 +676,7 @@ def cpu_baseline(Hq, Hkv, D, ctx, reps=2):
             "sample": f"unoptimized fp64 NumPy reference on {cores} host cores "
                       f"({blas_threads} BLAS threads): decode of one Llama-shaped layer "
                       f"(32/8 heads, hd128, e4m3 cache) at 1k/8k/32k/128k, best of {reps}; "
-                      f"quantize_rows on 4096 tokens; prefill_mirror on the last 4 rows of "
+                      f"quantize_rows on 4096 tokens; prefill_mirror on the last {prefill_rows} rows of "
                       f"the hd256 32k chunk; {total_s:.1f} s in all",
             "host_cores": cores, "blas_threads": blas_threads,
             "decode_ms": {str(c): round(decode_ms[c], 3) for c in ctxs},

@@ -16,8 +16,11 @@ shapes the GPU tests use, that
 The model follows the kernel source (csrc/prefill.hip): grid
 (ceil(max_q_len/128), H_q, B), blocks dispatched longest-first, key range
 [lo_key, hi_key] per workgroup, tiles t_lo .. t_hi, block ids of tiles t_lo
-and t_lo+1 before the loop and of tile t+2 inside step t, staged copies of
-tile t+1 inside step t (so one tile past t_hi is staged and never read).
+and t_lo+1 before the loop (clamped below to the window's first page) and of
+tile t+2 inside step t (clamped at the end only), staged copies of tile t+1
+inside step t (so one tile past t_hi is staged and never read), V rows
+zeroed before the window start in the prologue and past the end in the
+tail tile.
 """
 
 import pytest
@@ -49,19 +52,23 @@ def entries_read(seq_len, lo_key, t_lo, t_hi):
     n_pages = (seq_len + BLOCK - 1) // BLOCK
     pg_lo = lo_key // BLOCK
 
-    def page_blk(page):
-        return min(max(page, pg_lo), n_pages - 1)
+    def page_blk(page):                            # the end clamp
+        return page if page < n_pages else n_pages - 1
 
     idx = set()
-    for i in range(2 * ppt):                       # tiles t_lo, t_lo + 1
-        idx.add(page_blk((t_lo + i // ppt) * ppt + i % ppt))
+    for i in range(2 * ppt):                       # tiles t_lo, t_lo + 1 (prologue)
+        idx.add(page_blk(max((t_lo + i // ppt) * ppt + i % ppt, pg_lo)))
     t = t_lo
     while t <= t_hi:                               # loop unrolled by two
         for tt in (t, t + 1):
             if tt > t_hi:
                 break
             for i in range(ppt):                   # block ids of tile tt+2
-                idx.add(page_blk((tt + 2) * ppt + i))
+                page = (tt + 2) * ppt + i
+                # the loop applies no lower clamp: its pages lie above the
+                # window start by construction
+                assert page >= pg_lo, (page, pg_lo)
+                idx.add(page_blk(page))
         t += 2
     return idx
 
@@ -72,8 +79,10 @@ def zeroed_or_visible(seq_len, lo_key, hi_key, t):
     bad = []
     for r in range(KV_TILE):
         key = t * KV_TILE + r
-        zeroed = ((t + 1) * KV_TILE > seq_len or t * KV_TILE < lo_key) and \
-            (r < lo_key - t * KV_TILE or r >= seq_len - t * KV_TILE)
+        # the tail tile zeroes rows past the end; the prologue zeroes the
+        # rows of tile t_lo before the window start
+        zeroed = ((t + 1) * KV_TILE > seq_len and r >= seq_len - t * KV_TILE) or \
+            (t == lo_key // KV_TILE and r < lo_key - t * KV_TILE)
         visible = lo_key <= key <= hi_key and key < seq_len
         if not (zeroed or visible):
             # a key above hi_key but below seq_len is a real, written key
