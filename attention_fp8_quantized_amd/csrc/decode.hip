@@ -317,6 +317,16 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFmt>())) void decode
   const int n = lane & 15;     // key row (loads, K operand) / head (Q, S, P) / column (V, O)
   const int g = lane >> 4;     // k-group of the MFMA operands
 
+  // Without a window a split's page range starts at split * pages_per_split
+  // whatever the sequence length, so the block ids of this wave's first 64
+  // pages are requested together with the length instead of after it (one
+  // dependent round trip less before the first page).  Entries past the
+  // sequence end (inside the row) are read but never used.
+  const int32_t* bt = p.block_table + (size_t)b * p.max_blocks;
+  const bool early_ids = p.window <= 0 && p.max_blocks > 0;
+  int early_blk = 0;
+  if (early_ids)
+    early_blk = bt[min(split * p.pages_per_split + wave + NW * lane, p.max_blocks - 1)];
   const int L = p.seq_lens[b];
   const int lo = p.window > 0 ? max(0, L - p.window) : 0;
   const int page_lo = lo / kBlockSize;
@@ -353,7 +363,6 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFmt>())) void decode
 
   const uint8_t* head_base = p.cache + (size_t)h * 2 * HALF + n * ROW + 16 * g;
   const size_t blk_stride = (size_t)p.num_kv_heads * 2 * HALF;
-  const int32_t* bt = p.block_table + (size_t)b * p.max_blocks;
 
   struct Page {
     uint4 k[NL], v[NL];
@@ -596,7 +605,8 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFmt>())) void decode
   for (int jb = 0; jb < npw; jb += 64) {
     const int cnt = min(64, npw - jb);
     const int page_base = first + NW * jb;
-    const int my_blk = lane < cnt ? bt[page_base + NW * lane] : 0;
+    const int my_blk = (jb == 0 && early_ids) ? early_blk
+                                              : lane < cnt ? bt[page_base + NW * lane] : 0;
     auto blk_of = [&](int j) { return __builtin_amdgcn_readlane(my_blk, min(j, cnt - 1)); };
     Page ring[PD];
 #pragma unroll

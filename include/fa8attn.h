@@ -151,13 +151,15 @@ size_t fa8_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
  *   q            bf16 [batch][num_q_heads][head_dim]; query head hq reads
  *                KV head hq / (num_q_heads / num_kv_heads).
  *   block_table  int32 [batch][max_blocks_per_seq] physical block ids.
- *                Only the entries of pages that hold a visible key are read:
+ *                Only the entries of pages that hold a visible key are used:
  *                pages lo/16 .. (seq_lens[b]-1)/16 with lo the first key of
- *                the window (0 without one).  Entries outside the window may
- *                hold anything (a freed page, -1), and the cache rows of
- *                invisible keys (also the rows of a visible page before lo or
- *                past the end) may hold any bytes, NaN codes included: they
- *                never reach the output.
+ *                the window (0 without one).  With a window, no other entry
+ *                is read; without one, entries past the sequence end (within
+ *                the row) may be read early but are never used.  Unused
+ *                entries may hold anything (a freed page, -1), and the cache
+ *                rows of invisible keys (also the rows of a visible page
+ *                before lo or past the end) may hold any bytes, NaN codes
+ *                included: they never reach the output.
  *   seq_lens     int32 [batch]; the query is token seq_lens[b]-1, whose K/V
  *                must already be in the cache.  0 gives a zero output row.
  *   max_seq_len  host upper bound of seq_lens (sizes the grid only).
