@@ -81,9 +81,9 @@ int decode_pages_max(int max_seq_len, int window) {
 // ---- scratch of the allocation-free decode entry point ----------------------
 // Split partials and arrival counters of fa8_decode_attention_noalloc live in
 // this array instead of a caller's workspace: the first
-// FA8_DECODE_SCRATCH_COUNTERS int32 are the arrival counters (zero between
-// calls: cleared once per device, then re-armed by every call), the rest
-// holds the partials.  Each GPU the library runs on has its own copy, held
+// FA8_DECODE_SCRATCH_COUNTERS counters (each on its own 256-byte line, as in
+// a workspace) are the arrival counters (zero between calls: cleared once
+// per device, then re-armed by every call), the rest holds the partials.  Each GPU the library runs on has its own copy, held
 // until the process ends.  Host code never uses the name itself (it is a
 // host-side stand-in, not a device address): kernels and fills get the
 // per-device address hipGetSymbolAddress returns.
@@ -91,7 +91,7 @@ static __device__ __align__(256) unsigned char scratch[FA8_DECODE_SCRATCH_BYTES]
 
 namespace {
 
-constexpr size_t kScratchCounterBytes = (size_t)FA8_DECODE_SCRATCH_COUNTERS * 4;
+constexpr size_t kScratchCounterBytes = (size_t)FA8_DECODE_SCRATCH_COUNTERS * 4 * fa8::kCounterStride;
 constexpr int kMaxDevices = 64;
 
 struct ScratchSlot {
@@ -129,7 +129,7 @@ fa8_status scratch_for_call(hipStream_t stream, void** out) {
     e = hipStreamIsCapturing(stream, &cap);
     if (e != hipSuccess) return hip_fail(e, "decode_noalloc: hipStreamIsCapturing");
     hipLaunchKernelGGL(zero_words_kernel, dim3(16), dim3(256), 0, stream,
-                       reinterpret_cast<uint32_t*>(slot.ptr), FA8_DECODE_SCRATCH_COUNTERS);
+                       reinterpret_cast<uint32_t*>(slot.ptr), (int)(kScratchCounterBytes / 4));
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "decode_noalloc: counter clear launch");
     if (cap == hipStreamCaptureStatusNone) slot.cleared = true;

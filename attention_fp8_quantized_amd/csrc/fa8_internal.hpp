@@ -61,11 +61,15 @@ inline int decode_num_groups(int splits) {
   return splits <= kDecodeSingleLevel ? 1 : (splits + kDecodeFan - 1) / kDecodeFan;
 }
 
-// Decode workspace layout for `splits` splits (each array 16-byte aligned):
-// int32 arrival counters [B][Hq][NG] and [B][Hq] (zero before the first
-// call; every call leaves them zero), fp32 o_part [B][Hq][S][D], m and l
-// [B][Hq][S], and for NG > 1 the group partials o [B][Hq][NG][D], m, l
-// [B][Hq][NG].
+// Decode workspace layout for `splits` splits: int32 arrival counters
+// [B][Hq][NG] and [B][Hq], each kCounterStride ints apart (zero before the
+// first call; every call leaves them zero), fp32 o_part [B][Hq][S][D], m and
+// l [B][Hq][S], and for NG > 1 the group partials o [B][Hq][NG][D], m, l
+// [B][Hq][NG].  Every array starts 16-byte aligned when the workspace does.
+#ifndef FA8_COUNTER_STRIDE
+#define FA8_COUNTER_STRIDE 64
+#endif
+constexpr int kCounterStride = FA8_COUNTER_STRIDE;   // ints per counter (256 bytes)
 #ifndef FA8_DECODE_WAVES
 #define FA8_DECODE_WAVES 8
 #endif

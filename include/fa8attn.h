@@ -134,9 +134,11 @@ int32_t fa8_decode_num_splits(int32_t batch, int32_t num_kv_heads,
 
 /*
  * Bytes of device workspace fa8_decode_attention needs for `num_splits`
- * splits: one int32 arrival counter per (sequence, query head), then per
- * (sequence, query head, split) one unnormalised partial output row
- * (head_dim fp32) plus its running maximum and denominator (2 fp32).
+ * splits: int32 arrival counters (NG + 1 per sequence and query head, each
+ * on its own 256-byte line), then per (sequence, query head, split) one
+ * unnormalised partial output row (head_dim fp32) plus its running maximum
+ * and denominator (2 fp32), and for more than 64 splits the same for the
+ * NG = ceil(splits / 16) split groups (NG = 1 otherwise).
  */
 size_t fa8_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
                                   int32_t head_dim, int32_t num_splits);
@@ -206,7 +208,7 @@ fa8_status fa8_decode_attention(const void* q, int32_t batch,
  *   batch * num_q_heads * (NG + 1) <= FA8_DECODE_SCRATCH_COUNTERS, where
  *     NG = 1 for S <= 64, else ceil(S / 16), and
  *   fa8_decode_workspace_bytes(batch, num_q_heads, head_dim, S) minus the
- *     counters' 16-byte-aligned bytes <= FA8_DECODE_SCRATCH_BYTES - 4 *
+ *     counters' bytes (256 per counter) <= FA8_DECODE_SCRATCH_BYTES - 256 *
  *     FA8_DECODE_SCRATCH_COUNTERS
  *   (e.g. 32 query heads, head_dim 128, batch 8 and up to 100 splits fit).
  * Every call on a GPU shares that GPU's scratch, which keeps the last call's
@@ -218,7 +220,7 @@ fa8_status fa8_decode_attention(const void* q, int32_t batch,
  * clear in its graph until an eager call has done it).
  */
 #define FA8_DECODE_SCRATCH_BYTES (16u << 20)
-#define FA8_DECODE_SCRATCH_COUNTERS 16384
+#define FA8_DECODE_SCRATCH_COUNTERS 4096
 fa8_status fa8_decode_attention_noalloc(const void* q, int32_t batch,
                                         int32_t num_q_heads, const void* cache,
                                         int32_t cache_dtype, int64_t num_blocks,
