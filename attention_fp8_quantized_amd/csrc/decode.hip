@@ -352,14 +352,16 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFmt>())) void decode
 #pragma unroll
   for (int c = 0; c < NB; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // one LDS region: V slices during the loop, the wave merge afterwards
+  // two LDS regions: the per-wave V slices of the page loop, and the wave
+  // merge, which a wave fills as soon as its own loop ends (no barrier
+  // between the last page of one wave and another wave's merge writes)
   constexpr int kSliceBytes = kBlockSize * RS;
   // query heads merged per LDS round: all of them within a 64 KB budget
   constexpr int kMergeHeads = (65536 / (NW * D * 4)) < G ? (65536 / (NW * D * 4)) : G;
   constexpr int kMergeBytes = NW * kMergeHeads * D * 4 + 2 * NW * 16 * 4;
-  constexpr int kLdsBytes = NW * kSliceBytes > kMergeBytes ? NW * kSliceBytes : kMergeBytes;
-  __shared__ __attribute__((aligned(16))) uint8_t s_raw[kLdsBytes];
-  uint8_t* sv = s_raw + wave * kSliceBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t s_vsl[NW * kSliceBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_mrg[kMergeBytes];
+  uint8_t* sv = s_vsl + wave * kSliceBytes;
 
   const uint8_t* head_base = p.cache + (size_t)h * 2 * HALF + n * ROW + 16 * g;
   const size_t blk_stride = (size_t)p.num_kv_heads * 2 * HALF;
@@ -629,13 +631,12 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFmt>())) void decode
 
   // ---- merge the waves through LDS, kMergeHeads query heads per round -------
   l = cross_rows_sum(l);     // all keys of this wave, head n
-  float* s_o = reinterpret_cast<float*>(s_raw);                  // [NW][kMergeHeads][D]
+  float* s_o = reinterpret_cast<float*>(s_mrg);                  // [NW][kMergeHeads][D]
   float* s_m = s_o + NW * kMergeHeads * D;                       // [NW][16]
   float* s_l = s_m + NW * 16;                                    // [NW][16]
   const int S = p.num_splits;
   const float vsc = p.fp8 ? p.v_scale[h] : 1.0f;
   __shared__ int s_last;
-  __syncthreads();            // the V slices are dead from here on
   if (lane < 16) {
     s_m[wave * 16 + lane] = m;
     s_l[wave * 16 + lane] = l;
