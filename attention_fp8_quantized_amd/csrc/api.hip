@@ -208,16 +208,17 @@ int32_t fa8_decode_num_splits(int32_t batch, int32_t num_kv_heads, int32_t max_s
                               int32_t window) {
   const int pages = decode_pages_max(max_seq_len, window);
   if (batch <= 0 || num_kv_heads <= 0 || pages <= 0) return 1;
-  // Aim for one workgroup on 7/8 of the CUs (a decode workgroup fills a
-  // CU's register file), and at least one page per wave in every split.
-  // Each split pays a fixed chain (block ids, first pages, its share of the
-  // merge); measured on MI355X from 8k to 128k contexts, leaving 1/8 of the
-  // CUs idle but giving the others longer splits is as fast as or faster
-  // than one split per CU (e.g. 21.0 vs 21.5 us for a 32k, 8-KV-head layer;
-  // 18.1 vs 18.5 us for a 32k single-KV-head, head_dim-256 layer).
+  // One workgroup per CU (a decode workgroup fills a CU's register file):
+  // as many splits as fit the CUs beside the other (sequence, KV head) sets
+  // without a second round of workgroups, and at least one page per wave in
+  // every split.  Each split pays a fixed chain (block ids, first pages, its
+  // share of the merge).  Measured on MI355X with the arrival counters on
+  // separate lines: 32k Llama-shaped layer 19.9-20.0 us with 32 splits
+  // against 20.3 us with 28 (7/8 of the CUs); single-KV-head head_dim-256
+  // 128k layer 24.4 us with 256 splits against 24.6-25.4 us with 224.
   const int cus = device_cu_count();
-  const long target_wgs = (7L * cus) / 8;
-  long splits = (target_wgs + (long)batch * num_kv_heads - 1) / ((long)batch * num_kv_heads);
+  const long sets = (long)batch * num_kv_heads;
+  long splits = cus / sets;
   const long min_pages = fa8::kDecodeWaves;
   const long by_pages = pages / min_pages;
   if (splits > by_pages) splits = by_pages;
