@@ -801,14 +801,30 @@ void decode_workspace_carve(void* ws, int batch, int num_q_heads, int head_dim, 
                                batch, num_q_heads, head_dim, splits, p);
 }
 
-#ifndef FA8_DECODE_PIPE
-#define FA8_DECODE_PIPE 2      // pages in flight per wave
+// Pages in flight per wave, by head_dim.  At head_dim 256 a page-head is 8 KB
+// and a split has few pages per wave, so a two-deep ring asks for half of a
+// 67 MB layer at once and the first pages queue behind it; one page per wave
+// (64 KB per CU, as the two-deep ring at head_dim 128) measured faster:
+// 128k single-KV-head layer 24.45 -> 23.19 us, 32k 16.26 -> 14.90 us.  A
+// deeper ring at head_dim 64 (3 or 4 pages) measured 5-6% slower.
+#ifndef FA8_DECODE_PIPE_64
+#define FA8_DECODE_PIPE_64 2
 #endif
+#ifndef FA8_DECODE_PIPE_128
+#define FA8_DECODE_PIPE_128 2
+#endif
+#ifndef FA8_DECODE_PIPE_256
+#define FA8_DECODE_PIPE_256 1
+#endif
+template <int D>
+constexpr int decode_pipe() {
+  return D == 64 ? FA8_DECODE_PIPE_64 : D == 128 ? FA8_DECODE_PIPE_128 : FA8_DECODE_PIPE_256;
+}
 
 template <int D, int G, int kFmt>
 static void launch_shape(const DecodeParams& p, dim3 grid, hipStream_t stream) {
   constexpr int NW = kDecodeWaves;
-  hipLaunchKernelGGL((decode_split_kernel<D, G, kFmt, NW, FA8_DECODE_PIPE>), grid, dim3(64 * NW),
+  hipLaunchKernelGGL((decode_split_kernel<D, G, kFmt, NW, decode_pipe<D>()>), grid, dim3(64 * NW),
                      0, stream, p);
 }
 
