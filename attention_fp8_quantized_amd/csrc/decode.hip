@@ -801,17 +801,19 @@ void decode_workspace_carve(void* ws, int batch, int num_q_heads, int head_dim, 
                                batch, num_q_heads, head_dim, splits, p);
 }
 
-// Pages in flight per wave, by head_dim.  At head_dim 256 a page-head is 8 KB
-// and a split has few pages per wave, so a two-deep ring asks for half of a
-// 67 MB layer at once and the first pages queue behind it; one page per wave
-// (64 KB per CU, as the two-deep ring at head_dim 128) measured faster:
-// 128k single-KV-head layer 24.45 -> 23.19 us, 32k 16.26 -> 14.90 us.  A
-// deeper ring at head_dim 64 (3 or 4 pages) measured 5-6% slower.
+// Pages in flight per wave, by head_dim.  With one workgroup per CU a
+// two-deep ring asks for a large share of a layer at once (half of a 67 MB
+// head_dim-256 layer) and the first pages queue behind it; one page per wave
+// measured faster on MI355X: head_dim 256, 128k single-KV-head layer
+// 24.45 -> 23.19 us, 32k 16.26 -> 14.90 us; head_dim 128 (Llama-shaped),
+// 32k 19.80 -> 19.36 us, 128k 55.08 -> 53.45 us, 8 x 20k 64.45 -> 62.80 us
+// (8k 11.15 -> 11.28 us).  A deeper ring at head_dim 64 (3 or 4 pages)
+// measured 5-6% slower.
 #ifndef FA8_DECODE_PIPE_64
 #define FA8_DECODE_PIPE_64 2
 #endif
 #ifndef FA8_DECODE_PIPE_128
-#define FA8_DECODE_PIPE_128 2
+#define FA8_DECODE_PIPE_128 1
 #endif
 #ifndef FA8_DECODE_PIPE_256
 #define FA8_DECODE_PIPE_256 1
