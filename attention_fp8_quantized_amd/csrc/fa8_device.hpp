@@ -172,6 +172,60 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// fl32(x / s), the quotient correctly rounded, or the cheap product
+// q = fl32(x * r) (r = fl32(1 / s), correctly rounded; s positive and normal)
+// wherever q encodes to the same FP8 (kFmt) code.  |q - x/s| <= 2 ulp (r
+// carries at most half an ulp of relative error, the product rounding
+// another half), so q and the correctly rounded quotient lie in the same FP8
+// rounding interval unless q is within a few ulp of one of the format's
+// rounding midpoints, or in its subnormal range (whose midpoints sit at other
+// bit positions).  Only those elements divide exactly.  NaN and infinities
+// pass through the product as through the quotient.
+template <int kFmt>
+__device__ __forceinline__ float fp8_quotient(float x, float s, float r) {
+  // bits below the kept mantissa (3 bits e4m3, 2 bits e5m2), the midpoint
+  // pattern there, and the smallest normal value of the FP8 format
+  constexpr uint32_t kLow = kFmt == kFmtE5m2 ? 0x1FFFFFu : 0xFFFFFu;
+  constexpr uint32_t kMid = kFmt == kFmtE5m2 ? 0x100000u : 0x80000u;
+  constexpr uint32_t kMinNormal = kFmt == kFmtE5m2 ? 0x38800000u : 0x3C800000u;  // 2^-14 / 2^-6
+  constexpr uint32_t kWin = 16;   // ulp of margin on each side of a midpoint
+  float y = x * r;
+  const uint32_t a = __float_as_uint(y) & 0x7FFFFFFFu;
+  const bool near_mid = (a & kLow) - (kMid - kWin) <= 2 * kWin;
+  const bool fp8_subnormal = a - 1u < kMinNormal - 1u;   // 0 < |q| < min normal
+  if (near_mid || fp8_subnormal) {
+    // an opaque step, so that the compiler keeps this a branch instead of
+    // dividing every element and selecting
+    float xs = x;
+    asm volatile("" : "+v"(xs));
+    y = xs / s;
+  }
+  return y;
+}
+
+// Two FP8 codes (kFmt) of y0, y1 in the low 16 bits (y0 in bits 0-7): the
+// encoding of fp8_encode (round-to-nearest-even, saturation at the largest
+// finite value, +-inf included, NaN -> 0x7F with the input's sign, sign of
+// zero kept), done by the packed hardware conversion (nearest-even) on
+// values first clamped to the largest finite magnitude; NaN is set apart.
+template <int kFmt>
+__device__ __forceinline__ uint32_t fp8_encode2(float y0, float y1) {
+  constexpr uint32_t kMaxBits = kFmt == kFmtE5m2 ? 0x47600000u : 0x43E00000u;  // 57344 / 448
+  const uint32_t b0 = __float_as_uint(y0), b1 = __float_as_uint(y1);
+  const uint32_t a0 = b0 & 0x7FFFFFFFu, a1 = b1 & 0x7FFFFFFFu;
+  const float c0 = __uint_as_float(min(a0, kMaxBits) | (b0 & 0x80000000u));
+  const float c1 = __uint_as_float(min(a1, kMaxBits) | (b1 & 0x80000000u));
+  uint32_t w;
+  if constexpr (kFmt == kFmtE5m2)
+    w = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c0, c1, 0, false);
+  else
+    w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c0, c1, 0, false);
+  w &= 0xFFFFu;
+  if (a0 > 0x7F800000u) w = (w & 0xFF00u) | 0x7Fu | (b0 >> 24 & 0x80u);
+  if (a1 > 0x7F800000u) w = (w & 0x00FFu) | ((0x7Fu | (b1 >> 24 & 0x80u)) << 8);
+  return w;
+}
+
 // One 16-byte chunk of a cached row from its input elements (fp32 or bf16):
 // 16 FP8 codes (kFmt e4m3 or e5m2) of fl32(x / scale) (correctly rounded
 // quotient: callers are built without fast-math and with correctly rounded
@@ -207,13 +261,14 @@ __device__ __forceinline__ uint4 encode_chunk(const void* src, int64_t elem, flo
   }
   uint32_t packed[4];
   if constexpr (kFp8Cache) {
+    const float rcp = 1.0f / scale;   // correctly rounded, once per chunk
+    float y[N];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint32_t word = 0;
+    for (int i = 0; i < N; ++i) y[i] = fp8_quotient<kFmt>(x[i], scale, rcp);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) word |= fp8_encode<kFmt>(x[w * 4 + j] / scale) << (8 * j);
-      packed[w] = word;
-    }
+    for (int w = 0; w < 4; ++w)
+      packed[w] = fp8_encode2<kFmt>(y[4 * w], y[4 * w + 1]) |
+                  (fp8_encode2<kFmt>(y[4 * w + 2], y[4 * w + 3]) << 16);
   } else {
 #pragma unroll
     for (int w = 0; w < 4; ++w) packed[w] = bf16_bits(x[2 * w]) | (bf16_bits(x[2 * w + 1]) << 16);
