@@ -597,11 +597,10 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFmt>())) void decode
   };
 
   // This wave's pages: pg0 + wave + NW*j.  Block ids are fetched 64 at a
-  // time, one per lane, and broadcast with readlane.  Steady PD-deep ring:
-  // every buffer is consumed and re-issued in every round, and prefetches
-  // past the end repeat the last page (a cache hit), so every path keeps the
-  // same loads in flight and the compiler waits for exactly the page it is
-  // about to use.
+  // time, one per lane, and broadcast with readlane.  PD-deep ring: every
+  // buffer is consumed and re-issued in every steady round (prefetch indices
+  // past the batch end clamp to its last page), so the compiler waits for
+  // exactly the page about to be used; the last round issues nothing.
   const int first = pg0 + wave;
   const int npw = first < pg1 ? (pg1 - first + NW - 1) / NW : 0;
   for (int jb = 0; jb < npw; jb += 64) {
@@ -614,8 +613,11 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFmt>())) void decode
 #pragma unroll
     for (int k = 0; k < PD; ++k) issue(ring[k], blk_of(k));
     if (jb == 0 && owner) append_row();   // before any page is used
+    // steady rounds (straight-line: use each buffer, re-issue it), then the
+    // last round without re-issues: a load past the batch would hold its
+    // registers busy after the loop for data nobody reads
     int j = 0;
-    for (; j + PD <= cnt; j += PD) {
+    for (; j + PD < cnt; j += PD) {
 #pragma unroll
       for (int k = 0; k < PD; ++k) {
         run_page(ring[k], page_base + NW * (j + k));
@@ -625,7 +627,7 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFmt>())) void decode
       }
     }
 #pragma unroll
-    for (int k = 0; k < PD - 1; ++k)
+    for (int k = 0; k < PD; ++k)
       if (j + k < cnt) run_page(ring[k], page_base + NW * (j + k));
   }
 
