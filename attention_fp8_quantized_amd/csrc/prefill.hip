@@ -263,6 +263,11 @@ __global__ __launch_bounds__(64 * (8 / MB)) void prefill_kernel(PrefillParams p)
     const int r = (idx % CPT) * RPI + lane / (D / 16);            // tile row of the lane
     lane_off[par] = (r % kBlockSize) * D + ((lane % (D / 16)) ^ swz<D>(r)) * 16;
   }
+  // The copies are buffer loads with an LDS destination over one page's K
+  // or V rows: unlike the global (FLAT-encoded) form, which may also reach
+  // LDS through the flat aperture, they leave the compiler's LDS counter in
+  // order, so an operand read waits for its own data only instead of for
+  // every LDS read in flight.
   auto stage = [&](uint8_t* buf, int slot) {
     // opaque per call, so that the compiler keeps 32-bit lane offsets and
     // uniform page addresses instead of hoisting a 64-bit address per copy
@@ -276,8 +281,10 @@ __global__ __launch_bounds__(64 * (8 / MB)) void prefill_kernel(PrefillParams p)
       const int blk = __builtin_amdgcn_readfirstlane(s_bt[slot][row0 / kBlockSize]);
       const uint8_t* page = p.cache + (size_t)blk * blk_stride + head_off +
                             (size_t)kv * kBlockSize * D;
-      __builtin_amdgcn_global_load_lds(page + ((u & 1) ? voff1 : voff0),
-                                       (lds_void_ptr)(buf + kv * TILE + row0 * D), 16, 0, 0);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(page), 0, kBlockSize * D, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)(buf + kv * TILE + row0 * D), 16,
+                                               (u & 1) ? voff1 : voff0, 0, 0, 0);
     }
   };
 
