@@ -37,8 +37,8 @@
 //     tile leaves lane (n, g) with O[head 4g+i][16c + n].
 // The waves' states merge through LDS; each workgroup writes one
 // unnormalised partial (o, m, l) per query head, and the workgroup that
-// arrives last for its (sequence, KV head) merges the splits (in two levels
-// when there are many):
+// arrives last for its (sequence, KV head) merges the splits (with many
+// splits, the last arrivals share the merge, one slice of columns each):
 //   out = v_scale * sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
 // Empty splits carry m = -inf and weight 0; an all-empty row is 0.
 
@@ -142,22 +142,20 @@ __device__ __forceinline__ void st_agentv(__amdgpu_buffer_rsrc_t r, uint32_t byt
 // the merges keep all threads busy and issue the fewest requests.
 constexpr int ws_vec(int cols, int nt) { return cols >= 4 * nt ? 4 : cols >= 2 * nt ? 2 : 1; }
 
-// Merge n unnormalised partials (o, m, l) of each of GW query heads, run by
-// one workgroup.  Head g's partial rows are rows r0 .. r0+n-1 of a block of
-// `rows` rows starting at (head g) * rows:
-//   M = max_i m_i,  w_i = 2^(m_i - M),  o = sum_i w_i o_i,  l = sum_i w_i l_i.
-// kFinal: out[g][d] = v_scale * o / l (0 when every partial is empty);
-// otherwise the merged partial (o, M, l) is stored at row `dst_row` of a
-// block of `dst_rows` rows per head.  Each thread owns V consecutive
-// columns (one load of V floats per partial row); R adjacent lanes share
-// them and take every R-th row.  All partial loads of a batch are issued
-// before any is used, and the first batch is in flight while the maxima are
-// reduced.
-template <int D, int GW, int NW, bool kFinal>
+// Merge the n (<= kDecodeSingleLevel) unnormalised partials (o, m, l) of
+// each of GW query heads into the output, run by one workgroup.  Head g's
+// partial rows are rows 0 .. n-1 of a block of n rows starting at (head g) * n:
+//   M = max_i m_i,  w_i = 2^(m_i - M),
+//   out[g][d] = v_scale * sum_i w_i o_i[d] / sum_i w_i l_i  (0 when every
+//   partial is empty).
+// Each thread owns V consecutive columns (one load of V floats per partial
+// row); R adjacent lanes share them and take every R-th row.  All partial
+// loads of a batch are issued before any is used, and the first batch is in
+// flight while the maxima are reduced.
+template <int D, int GW, int NW>
 __device__ __forceinline__ void merge_rows(const float* o_in, const float* m_in,
-                                           const float* l_in, int rows, int r0, int n,
-                                           float* o_dst, float* m_dst, float* l_dst,
-                                           int dst_rows, int dst_row, float vsc) {
+                                           const float* l_in, int n, float* o_dst, float vsc) {
+  const int rows = n, r0 = 0;
   constexpr int NT = 64 * NW;
   constexpr int V = ws_vec(GW * D, NT);               // columns per load
   constexpr int CG = GW * D / V;                      // V-column groups of the output
@@ -260,22 +258,117 @@ __device__ __forceinline__ void merge_rows(const float* o_in, const float* m_in,
     const int g = col / (D / V);
     const int d = (col % (D / V)) * V;
     if (r == 0) {
-      if constexpr (kFinal) {
-        const float f = vsc / s_den[g];
+      const float f = vsc / s_den[g];
 #pragma unroll
-        for (int c = 0; c < V; ++c) o_dst[(size_t)g * D + d + c] = s_mx[g] > kNegInf ? a[c] * f : 0.f;
-      } else {
-        const int row = g * dst_rows + dst_row;
-        st_agentv<V>(ws_rsrc(o_dst, (uint32_t)(GW * dst_rows * D * 4)), (uint32_t)(row * D + d) * 4, a);
-        if (d == 0) {
-          st_agent(m_dst + (size_t)row, s_mx[g]);
-          st_agent(l_dst + (size_t)row, s_den[g]);
-        }
-      }
+      for (int c = 0; c < V; ++c) o_dst[(size_t)g * D + d + c] = s_mx[g] > kNegInf ? a[c] * f : 0.f;
     }
   }
 }
 
+
+// Polls of the set counter by a slice merger waiting for the last split
+// group (each poll is an agent-scope load plus a short sleep; the bound is
+// far beyond any real wait, so that the kernel ends even if a split never
+// came).
+constexpr int kMergeWaitPolls = 1 << 20;
+
+// Merge all n (<= kDecodeMaxSplits) partial rows of one query head over the
+// 64 output columns c0 .. c0+63, run by one workgroup of NW waves:
+//   M = max_i m_i,  w_i = 2^(m_i - M),
+//   out[c] = v_scale * sum_i w_i o_i[c] / sum_i w_i l_i  (0 when every
+//   partial is empty).
+// The head's partial rows are rows 0 .. n-1 of o_head ([n][D]).  Lane l of
+// wave w owns the four columns 4 (l % 16) .. +3 of rows 4w + l/16 + 4 NW j,
+// so that one load instruction covers four whole 256-byte row slices (the
+// loads bypass the caches: rows scattered over the lanes would fetch each
+// line four times).  All partial loads are issued before the weights are
+// waited for; the row sums meet through lane shuffles and an LDS array.
+template <int D, int NW>
+__device__ __forceinline__ void merge_slice(const float* o_head, const float* m_head,
+                                            const float* l_head, int n, int c0,
+                                            float* out_head, float vsc) {
+  constexpr int NT = 64 * NW;
+  constexpr int RP = 4 * NW;                          // rows per pass of all waves
+  constexpr int JR = (kDecodeMaxSplits + RP - 1) / RP; // passes (rows per lane) at most
+  constexpr int MK = kDecodeMaxSplits / 64;           // rows per lane of the weight wave
+  static_assert(D % 64 == 0, "64-column slices");
+  __shared__ float s_w[kDecodeMaxSplits];
+  __shared__ float s_lw[kDecodeMaxSplits];
+  __shared__ f32x4 s_part[NW][16];
+  __shared__ float s_mx, s_den;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int cg = lane & 15;                           // four-column group
+  const int rp = 4 * wave + (lane >> 4);              // first row of the lane
+  const __amdgpu_buffer_rsrc_t src = ws_rsrc(o_head, (uint32_t)(n * D * 4));
+  f32x4 v[JR];
+#pragma unroll
+  for (int j = 0; j < JR; ++j) {
+    const int i = min(rp + j * RP, n - 1);   // rows past n repeat row n-1, never used
+    v[j] = ld_agentv<4>(src, (uint32_t)(i * D + c0 + 4 * cg) * 4);
+  }
+  for (int i = t; i < n; i += NT) {
+    s_w[i] = ld_agent(m_head + i);
+    s_lw[i] = ld_agent(l_head + i);
+  }
+  __syncthreads();
+  if (t < 64) {   // one wave: the maximum, the weights and the denominator
+    float mk[MK];
+    float M = kNegInf;
+#pragma unroll
+    for (int k = 0; k < MK; ++k) {
+      const int i = t + 64 * k;
+      mk[k] = i < n ? s_w[i] : kNegInf;
+      M = fmaxf(M, mk[k]);
+    }
+    M = wave_max(M);
+    float den = 0.f;
+#pragma unroll
+    for (int k = 0; k < MK; ++k) {
+      const int i = t + 64 * k;
+      const float f = (M > kNegInf && mk[k] > kNegInf) ? fast_exp2(mk[k] - M) : 0.f;
+      if (i < n) {
+        s_w[i] = f;
+        den += f * s_lw[i];
+      }
+    }
+    den = wave_sum(den);
+    if (t == 0) {
+      s_mx = M;
+      s_den = den;
+    }
+  }
+  __syncthreads();
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < JR; ++j) {
+    const int i = rp + j * RP;
+    if (i < n) {
+      const float w = s_w[i];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] += w * v[j][c];
+    }
+  }
+  // the four lanes of this column group in the wave (l, l^16, l^32, l^48)
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    acc[c] += __shfl_xor(acc[c], 16);
+    acc[c] += __shfl_xor(acc[c], 32);
+  }
+  if (lane < 16) s_part[wave][lane] = acc;
+  __syncthreads();
+  if (t < 16) {
+    f32x4 a = s_part[0][t];
+#pragma unroll
+    for (int w = 1; w < NW; ++w)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) a[c] += s_part[w][t][c];
+    const float f = vsc / s_den;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) out_head[c0 + 4 * t + c] = s_mx > kNegInf ? a[c] * f : 0.f;
+  }
+}
 
 // 8 FP8 codes (two dwords) -> 8 bf16 (exact for e4m3 and e5m2)
 template <int kFmt>
@@ -699,51 +792,81 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFmt>())) void decode
   }
   if (S == 1) return;   // no partials, no arrival count, no merge
 
-  // ---- the last workgroup of this (sequence, head group) merges the splits -
+  // ---- the last workgroups of this (sequence, head group) merge the splits --
   // Each thread waits until its partial stores are performed (they are
-  // coherent agent-scope stores), then the workgroup counts its arrival.  With
-  // one split group the last arrival merges all splits into the output; with
-  // several, the last arrival of each group merges the group into a group
-  // partial and counts at the second level, whose last arrival merges the
-  // group partials.  Each merger re-arms its counter for the next call.  No
-  // workgroup waits for another.
+  // coherent agent-scope stores), then the workgroup counts its arrival.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const int NG = p.num_groups;
-  const int grp = split / p.group_size;
-  const int gr0 = grp * p.group_size;
-  const int gn = min(p.group_size, S - gr0);
   const size_t set = (size_t)b * gridDim.y + blockIdx.y;
-  int* counter = p.ws_count + (set * NG + grp) * kCounterStride;
-  if (threadIdx.x == 0)
-    s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gn - 1;
-  __syncthreads();
-  if (!s_last) return;
   const size_t head0 = (size_t)b * p.num_q_heads + hq0;   // first query head of the set
   if (NG == 1) {
-    merge_rows<D, G, NW, true>(p.ws_o + head0 * S * D, p.ws_m + head0 * S,
-                                p.ws_l + head0 * S,
-                                S, 0, S, p.out + head0 * D, nullptr, nullptr, 0, 0, vsc);
+    // up to kDecodeSingleLevel splits: the last arrival merges them all into
+    // the output and re-arms the counter for the next call
+    int* counter = p.ws_count + set * kCounterStride;
+    if (threadIdx.x == 0)
+      s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+    __syncthreads();
+    if (!s_last) return;
+    merge_rows<D, G, NW>(p.ws_o + head0 * S * D, p.ws_m + head0 * S, p.ws_l + head0 * S, S,
+                         p.out + head0 * D, vsc);
     if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
-  merge_rows<D, G, NW, false>(p.ws_o + head0 * S * D, p.ws_m + head0 * S,
-                               p.ws_l + head0 * S, S, gr0, gn,
-                               p.ws_o1 + head0 * NG * D, p.ws_m1 + head0 * NG,
-                               p.ws_l1 + head0 * NG, NG, grp, vsc);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  int* counter2 = p.ws_count2 + set * kCounterStride;
+  // More splits: arrivals count per group of kDecodeFan splits, each group
+  // counter on a line of its own (the arrivals of a launch would serialise
+  // at the memory's atomic unit on a single line).  The last arrival of a
+  // group re-arms its group counter and counts the group on the set counter.
+  // The last mpg arrivals of every group merge, one slice of 64 output
+  // columns of one query head at a time, over all S partials, instead of one
+  // workgroup reading every partial.  A merger that did not see the set
+  // counter reach NG itself waits for it (a bounded wait: the splits still
+  // to arrive are running, or start on the CUs the earlier arrivals have
+  // left).  The last merger to finish re-arms the set counter and the done
+  // counter for the next call; it does so only after every merger has seen
+  // the full count.
+  constexpr int NSL = G * D / 64;                 // output slices of the set
+  const int grp = split / kDecodeFan;
+  const int gn = min(kDecodeFan, S - grp * kDecodeFan);      // splits of this group
+  const int gn_last = S - (NG - 1) * kDecodeFan;
+  const int mpg = (NSL + NG - 1) / NG;            // mergers per full group (<= kDecodeFan)
+  const int nm = (NG - 1) * mpg + min(gn_last, mpg);          // mergers in all
+  int* gcount = p.ws_count + (set * NG + grp) * kCounterStride;
+  int* scount = p.ws_count2 + (set * 2) * kCounterStride;
+  int* done = p.ws_count2 + (set * 2 + 1) * kCounterStride;
+  __shared__ int s_all;
   if (threadIdx.x == 0) {
-    __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = __hip_atomic_fetch_add(counter2, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == NG - 1;
+    const int ticket = __hip_atomic_fetch_add(gcount, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int all = 0;
+    if (ticket == gn - 1) {
+      __hip_atomic_store(gcount, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      all = __hip_atomic_fetch_add(scount, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == NG - 1;
+    }
+    s_last = ticket;
+    s_all = all;
   }
   __syncthreads();
-  if (!s_last) return;
-  merge_rows<D, G, NW, true>(p.ws_o1 + head0 * NG * D, p.ws_m1 + head0 * NG,
-                              p.ws_l1 + head0 * NG, NG, 0, NG, p.out + head0 * D, nullptr,
-                              nullptr, 0, 0, vsc);
-  if (threadIdx.x == 0) __hip_atomic_store(counter2, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int k = s_last - (gn - min(gn, mpg));     // merger index within the group
+  if (k < 0) return;
+  if (threadIdx.x == 0 && !s_all) {
+    for (int it = 0; it < kMergeWaitPolls; ++it) {
+      if (__hip_atomic_load(scount, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= NG) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __syncthreads();
+  for (int sl = grp * mpg + k; sl < NSL; sl += nm) {
+    const int g = sl / (D / 64);
+    merge_slice<D, NW>(p.ws_o + (head0 + g) * S * D, p.ws_m + (head0 + g) * S,
+                       p.ws_l + (head0 + g) * S, S, (sl % (D / 64)) * 64,
+                       p.out + (head0 + g) * D, vsc);
+    __syncthreads();   // the slice's LDS is reused by the next one
+  }
+  if (threadIdx.x == 0 &&
+      __hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nm - 1) {
+    __hip_atomic_store(scount, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 static size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
@@ -756,15 +879,13 @@ static size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 // line too measured 0.2-0.4 us slower, the merger then fetches more lines).
 size_t decode_counter_bytes(int batch, int num_q_heads, int splits) {
   const size_t heads = (size_t)batch * num_q_heads;
-  return heads * (decode_num_groups(splits) + 1) * kCounterStride * 4;
+  const int ng = decode_num_groups(splits);
+  return heads * (ng + (ng > 1 ? 2 : 1)) * kCounterStride * 4;
 }
 
 size_t decode_partial_bytes(int batch, int num_q_heads, int head_dim, int splits) {
   const size_t heads = (size_t)batch * num_q_heads;
-  const int ng = decode_num_groups(splits);
-  size_t n = align16(heads * splits * head_dim * 4) + 2 * align16(heads * splits * 4);
-  if (ng > 1) n += align16(heads * ng * head_dim * 4) + 2 * align16(heads * ng * 4);
-  return n;
+  return align16(heads * splits * head_dim * 4) + 2 * align16(heads * splits * 4);
 }
 
 size_t decode_workspace_bytes(int batch, int num_q_heads, int head_dim, int splits) {
@@ -784,15 +905,6 @@ void decode_workspace_carve_split(int* counters, void* partials, int batch, int 
   p.ws_m = reinterpret_cast<float*>(at);
   at += align16(heads * splits * 4);
   p.ws_l = reinterpret_cast<float*>(at);
-  at += align16(heads * splits * 4);
-  p.ws_o1 = p.ws_m1 = p.ws_l1 = nullptr;
-  if (ng > 1) {
-    p.ws_o1 = reinterpret_cast<float*>(at);
-    at += align16(heads * ng * head_dim * 4);
-    p.ws_m1 = reinterpret_cast<float*>(at);
-    at += align16(heads * ng * 4);
-    p.ws_l1 = reinterpret_cast<float*>(at);
-  }
 }
 
 void decode_workspace_carve(void* ws, int batch, int num_q_heads, int head_dim, int splits,

@@ -33,27 +33,24 @@ struct DecodeParams {
   const float* k_scale;       // [Hkv]
   const float* v_scale;       // [Hkv]
   int* ws_count;              // group arrival counters [B][Hq][NG], zero between calls
-  int* ws_count2;             // second-level counters [B][Hq], zero between calls
+  int* ws_count2;             // NG > 1: set and merger counters [B][Hq][2], zero between calls
   float* ws_o;                // [B][Hq][S][D]
   float* ws_m;                // [B][Hq][S]  (log2 domain)
   float* ws_l;                // [B][Hq][S]
-  float* ws_o1;               // [B][Hq][NG][D] group partials (NG > 1 only)
-  float* ws_m1;               // [B][Hq][NG]
-  float* ws_l1;               // [B][Hq][NG]
   float* out;                 // [B][Hq][D]
   const void* k_new;          // fused append: [B][Hkv][D] row of token seq_len-1 (or null)
   const void* v_new;
   int new_bf16;               // fused append input: bf16 (1) or fp32 (0)
   int batch, num_q_heads, num_kv_heads, head_dim, max_blocks;
   int num_splits, pages_per_split, window, fp8;
-  int num_groups, group_size; // split groups merged first (1 group: single level)
+  int num_groups, group_size; // split groups of the arrival count (1 group: single merger)
   float sm_scale;
 };
 
-// Splits are merged in one level when there are at most kDecodeSingleLevel
-// of them; beyond that, groups of kDecodeFan splits are merged first (by
-// the last workgroup of each group) and the group results then (by the
-// last group merger), so no workgroup merges more than 64 partials.
+// Splits are merged by the last workgroup to arrive when there are at most
+// kDecodeSingleLevel of them; beyond that, arrivals are counted per group of
+// kDecodeFan splits and the merge is spread over the last arrivals of every
+// group, one slice of 64 output columns each (decode.hip).
 constexpr int kDecodeMaxSplits = 256;
 constexpr int kDecodeSingleLevel = 64;
 constexpr int kDecodeFan = 16;
@@ -62,10 +59,10 @@ inline int decode_num_groups(int splits) {
 }
 
 // Decode workspace layout for `splits` splits: int32 arrival counters
-// [B][Hq][NG] and [B][Hq], each kCounterStride ints apart (zero before the
-// first call; every call leaves them zero), fp32 o_part [B][Hq][S][D], m and
-// l [B][Hq][S], and for NG > 1 the group partials o [B][Hq][NG][D], m, l
-// [B][Hq][NG].  Every array starts 16-byte aligned when the workspace does.
+// [B][Hq][NG] and then [B][Hq] (NG = 1) or [B][Hq][2] (NG > 1: the set and
+// merger counters), each kCounterStride ints apart (zero before the first
+// call; every call leaves them zero), then fp32 o_part [B][Hq][S][D], m and
+// l [B][Hq][S].  Every array starts 16-byte aligned when the workspace does.
 #ifndef FA8_COUNTER_STRIDE
 #define FA8_COUNTER_STRIDE 64
 #endif

@@ -134,11 +134,11 @@ int32_t fa8_decode_num_splits(int32_t batch, int32_t num_kv_heads,
 
 /*
  * Bytes of device workspace fa8_decode_attention needs for `num_splits`
- * splits: int32 arrival counters (NG + 1 per sequence and query head, each
- * on its own 256-byte line), then per (sequence, query head, split) one
- * unnormalised partial output row (head_dim fp32) plus its running maximum
- * and denominator (2 fp32), and for more than 64 splits the same for the
- * NG = ceil(splits / 16) split groups (NG = 1 otherwise).
+ * splits: int32 arrival counters, each on its own 256-byte line (2 per
+ * sequence and query head for up to 64 splits; beyond, NG + 2 with
+ * NG = ceil(splits / 16) split groups), then per (sequence, query head,
+ * split) one unnormalised partial output row (head_dim fp32) plus its running
+ * maximum and denominator (2 fp32).
  */
 size_t fa8_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
                                   int32_t head_dim, int32_t num_splits);
@@ -205,8 +205,8 @@ fa8_status fa8_decode_attention(const void* q, int32_t batch,
  * library routine).
  * Limits (FA8_EINVAL beyond them, before anything is launched), with S the
  * split count (num_splits, or fa8_decode_num_splits(...) when 0):
- *   batch * num_q_heads * (NG + 1) <= FA8_DECODE_SCRATCH_COUNTERS, where
- *     NG = 1 for S <= 64, else ceil(S / 16), and
+ *   batch * num_q_heads * C <= FA8_DECODE_SCRATCH_COUNTERS, where
+ *     C = 2 for S <= 64, else ceil(S / 16) + 2, and
  *   fa8_decode_workspace_bytes(batch, num_q_heads, head_dim, S) minus the
  *     counters' bytes (256 per counter) <= FA8_DECODE_SCRATCH_BYTES - 256 *
  *     FA8_DECODE_SCRATCH_COUNTERS

@@ -51,24 +51,21 @@ def test_kv_tile_contract(lib):
 
 
 def _ws_expected(B, Hq, D, S):
-    """Documented layout: int32 counters B*Hq*(NG+1), each on a 256-byte
-    line; fp32 o_part B*Hq*S*D, m and l B*Hq*S (each array 16-byte aligned);
-    for S > 64 the group partials B*Hq*NG*(D+2) with NG = ceil(S/16)."""
+    """Documented layout: int32 counters B*Hq*C, each on a 256-byte line,
+    with C = 2 for S <= 64 and ceil(S/16) + 2 beyond; fp32 o_part
+    B*Hq*S*D, m and l B*Hq*S (each array 16-byte aligned)."""
     a16 = lambda x: (x + 15) // 16 * 16  # noqa: E731
-    ng = 1 if S <= 64 else -(-S // 16)
-    n = B * Hq * (ng + 1) * 256 + a16(B * Hq * S * D * 4) + 2 * a16(B * Hq * S * 4)
-    if ng > 1:
-        n += a16(B * Hq * ng * D * 4) + 2 * a16(B * Hq * ng * 4)
-    return n
+    c = 2 if S <= 64 else -(-S // 16) + 2
+    return B * Hq * c * 256 + a16(B * Hq * S * D * 4) + 2 * a16(B * Hq * S * 4)
 
 
 def test_workspace_size(lib):
     assert lib.fa8_decode_workspace_bytes(1, 32, 128, 64) == \
         32 * 2 * 256 + 32 * 64 * 128 * 4 + 2 * 32 * 64 * 4
     assert lib.fa8_decode_workspace_bytes(1, 1, 64, 1) == 2 * 256 + 256 + 16 + 16
-    # 256 splits: 16 groups of 16
+    # 256 splits: 16 group counters + the set and merger counters
     assert lib.fa8_decode_workspace_bytes(1, 8, 256, 256) == \
-        8 * 17 * 256 + 8 * 256 * 256 * 4 + 2 * 8 * 256 * 4 + 8 * 16 * 256 * 4 + 2 * 8 * 16 * 4
+        8 * 18 * 256 + 8 * 256 * 256 * 4 + 2 * 8 * 256 * 4
     for B, Hq, D, S in [(3, 5, 64, 65), (2, 7, 128, 100), (1, 1, 256, 250), (8, 64, 64, 2)]:
         assert lib.fa8_decode_workspace_bytes(B, Hq, D, S) == _ws_expected(B, Hq, D, S)
     assert lib.fa8_decode_workspace_bytes(0, 1, 64, 1) == 0
@@ -179,7 +176,7 @@ def test_decode_noalloc_rejects_bad_arguments_and_oversized_layouts(lib):
     assert _decode_noalloc(lib, splits=257) == EINVAL
     assert _decode_noalloc(lib, B=0) == 0                    # empty batch: no-op
     # ... and layouts beyond the fixed scratch: 64 x 16 heads x 256 splits
-    # of 256 floats need 287 MB of partials (and 17,408 counters)
+    # of 256 floats need 270 MB of partials (and 18,432 counters)
     assert _decode_noalloc(lib, B=64, Hq=16, Hkv=1, D=256, splits=256) == EINVAL
     assert b"scratch" in lib.fa8_last_error()
     # partials alone too large: 8 x 32 heads x 256 splits x 128 floats
