@@ -272,35 +272,48 @@ __device__ __forceinline__ void merge_rows(const float* o_in, const float* m_in,
 // came).
 constexpr int kMergeWaitPolls = 1 << 20;
 
+#ifndef FA8_MERGE_SLICE_COLS
+#define FA8_MERGE_SLICE_COLS 128
+#endif
+// Output columns per slice merger (a power of two from 16 to 256; capped at
+// head_dim).  Measured on MI355X, single-KV-head head_dim-256 layer with 8
+// query heads and 256 splits, 128k / 32k context: 16 columns 23.64 / 15.85
+// us, 32: 22.60 / 14.66, 64: 22.08 / 14.05, 128: 21.77 / 13.80 (16
+// mergers, one per split group), 256: 23.50 / 15.68.
+constexpr int kSliceCols = FA8_MERGE_SLICE_COLS;
+
 // Merge all n (<= kDecodeMaxSplits) partial rows of one query head over the
-// 64 output columns c0 .. c0+63, run by one workgroup of NW waves:
+// SW output columns c0 .. c0+SW-1, run by one workgroup of NW waves:
 //   M = max_i m_i,  w_i = 2^(m_i - M),
 //   out[c] = v_scale * sum_i w_i o_i[c] / sum_i w_i l_i  (0 when every
 //   partial is empty).
-// The head's partial rows are rows 0 .. n-1 of o_head ([n][D]).  Lane l of
-// wave w owns the four columns 4 (l % 16) .. +3 of rows 4w + l/16 + 4 NW j,
-// so that one load instruction covers four whole 256-byte row slices (the
-// loads bypass the caches: rows scattered over the lanes would fetch each
-// line four times).  All partial loads are issued before the weights are
-// waited for; the row sums meet through lane shuffles and an LDS array.
-template <int D, int NW>
+// The head's partial rows are rows 0 .. n-1 of o_head ([n][D]).  Lane l of a
+// wave owns the four columns 4 (l % CG) .. +3 (CG = SW / 4) of one
+// row, the wave's lanes covering 64 / CG consecutive rows, so that one load
+// instruction covers whole row slices (the loads bypass the caches: rows
+// scattered over the lanes would fetch each line several times).  All
+// partial loads are issued before the weights are waited for; the row sums
+// meet through lane shuffles and an LDS array.
+template <int D, int NW, int SW>
 __device__ __forceinline__ void merge_slice(const float* o_head, const float* m_head,
                                             const float* l_head, int n, int c0,
                                             float* out_head, float vsc) {
   constexpr int NT = 64 * NW;
-  constexpr int RP = 4 * NW;                          // rows per pass of all waves
+  constexpr int CG = SW / 4;                          // four-column groups of the slice
+  constexpr int RW = 64 / CG;                         // rows per wave per pass
+  constexpr int RP = RW * NW;                         // rows per pass of all waves
   constexpr int JR = (kDecodeMaxSplits + RP - 1) / RP; // passes (rows per lane) at most
   constexpr int MK = kDecodeMaxSplits / 64;           // rows per lane of the weight wave
-  static_assert(D % 64 == 0, "64-column slices");
+  static_assert(CG >= 4 && CG <= 64 && (CG & (CG - 1)) == 0, "slice width");
   __shared__ float s_w[kDecodeMaxSplits];
   __shared__ float s_lw[kDecodeMaxSplits];
-  __shared__ f32x4 s_part[NW][16];
+  __shared__ f32x4 s_part[NW][CG];
   __shared__ float s_mx, s_den;
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
-  const int cg = lane & 15;                           // four-column group
-  const int rp = 4 * wave + (lane >> 4);              // first row of the lane
+  const int cg = lane % CG;                           // four-column group
+  const int rp = RW * wave + lane / CG;               // first row of the lane
   const __amdgpu_buffer_rsrc_t src = ws_rsrc(o_head, (uint32_t)(n * D * 4));
   f32x4 v[JR];
 #pragma unroll
@@ -350,15 +363,14 @@ __device__ __forceinline__ void merge_slice(const float* o_head, const float* m_
       for (int c = 0; c < 4; ++c) acc[c] += w * v[j][c];
     }
   }
-  // the four lanes of this column group in the wave (l, l^16, l^32, l^48)
+  // the RW lanes of this column group in the wave (l ^ CG, l ^ 2CG, ...)
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    acc[c] += __shfl_xor(acc[c], 16);
-    acc[c] += __shfl_xor(acc[c], 32);
-  }
-  if (lane < 16) s_part[wave][lane] = acc;
+  for (int x = CG; x < 64; x *= 2)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] += __shfl_xor(acc[c], x);
+  if (lane < CG) s_part[wave][lane] = acc;
   __syncthreads();
-  if (t < 16) {
+  if (t < CG) {
     f32x4 a = s_part[0][t];
 #pragma unroll
     for (int w = 1; w < NW; ++w)
@@ -817,7 +829,7 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFmt>())) void decode
   // counter on a line of its own (the arrivals of a launch would serialise
   // at the memory's atomic unit on a single line).  The last arrival of a
   // group re-arms its group counter and counts the group on the set counter.
-  // The last mpg arrivals of every group merge, one slice of 64 output
+  // The last mpg arrivals of every group merge, one slice of SW output
   // columns of one query head at a time, over all S partials, instead of one
   // workgroup reading every partial.  A merger that did not see the set
   // counter reach NG itself waits for it (a bounded wait: the splits still
@@ -825,11 +837,12 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFmt>())) void decode
   // left).  The last merger to finish re-arms the set counter and the done
   // counter for the next call; it does so only after every merger has seen
   // the full count.
-  constexpr int NSL = G * D / 64;                 // output slices of the set
+  constexpr int SW = kSliceCols < D ? kSliceCols : D;   // columns per slice
+  constexpr int NSL = G * D / SW;                 // output slices of the set
   const int grp = split / kDecodeFan;
   const int gn = min(kDecodeFan, S - grp * kDecodeFan);      // splits of this group
   const int gn_last = S - (NG - 1) * kDecodeFan;
-  const int mpg = (NSL + NG - 1) / NG;            // mergers per full group (<= kDecodeFan)
+  const int mpg = min((NSL + NG - 1) / NG, kDecodeFan);      // mergers per full group
   const int nm = (NG - 1) * mpg + min(gn_last, mpg);          // mergers in all
   int* gcount = p.ws_count + (set * NG + grp) * kCounterStride;
   int* scount = p.ws_count2 + (set * 2) * kCounterStride;
@@ -856,10 +869,10 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFmt>())) void decode
   }
   __syncthreads();
   for (int sl = grp * mpg + k; sl < NSL; sl += nm) {
-    const int g = sl / (D / 64);
-    merge_slice<D, NW>(p.ws_o + (head0 + g) * S * D, p.ws_m + (head0 + g) * S,
-                       p.ws_l + (head0 + g) * S, S, (sl % (D / 64)) * 64,
-                       p.out + (head0 + g) * D, vsc);
+    const int g = sl / (D / SW);
+    merge_slice<D, NW, SW>(p.ws_o + (head0 + g) * S * D, p.ws_m + (head0 + g) * S,
+                           p.ws_l + (head0 + g) * S, S, (sl % (D / SW)) * SW,
+                           p.out + (head0 + g) * D, vsc);
     __syncthreads();   // the slice's LDS is reused by the next one
   }
   if (threadIdx.x == 0 &&
