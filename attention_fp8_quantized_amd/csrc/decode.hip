@@ -832,9 +832,12 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFmt>())) void decode
   // The last mpg arrivals of every group merge, one slice of SW output
   // columns of one query head at a time, over all S partials, instead of one
   // workgroup reading every partial.  A merger that did not see the set
-  // counter reach NG itself waits for it (a bounded wait: the splits still
-  // to arrive are running, or start on the CUs the earlier arrivals have
-  // left).  The last merger to finish re-arms the set counter and the done
+  // counter reach NG itself waits for it.  The wait ends: workgroups are
+  // dispatched in grid order, so every split of an earlier set has started
+  // and will finish, the splits of this set that have not arrived are running
+  // or start on the CUs that other workgroups leave, and at most nm (<= 64)
+  // workgroups of a set wait at a time; the poll count is bounded all the
+  // same.  The last merger to finish re-arms the set counter and the done
   // counter for the next call; it does so only after every merger has seen
   // the full count.
   constexpr int SW = kSliceCols < D ? kSliceCols : D;   // columns per slice

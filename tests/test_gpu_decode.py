@@ -82,12 +82,13 @@ def test_split_count_invariance(cd):
 
 
 @pytest.mark.parametrize("D,G", [(256, 4), (128, 8), (64, 16), (256, 16), (128, 16)])
-def test_two_level_merge_access_widths(D, G):
-    # The merges move partials 4, 8 or 16 bytes per lane, chosen from the
-    # G*D outputs of a (sequence, KV head) set: 8 bytes for G*D = 1024,
-    # 16 bytes for 2048, and 16 bytes with two column groups per thread for
-    # 4096.  Beyond 64 splits the merge runs in two levels; with 250 splits
-    # the shorter sequence leaves most splits empty.
+def test_many_split_merge_widths(D, G):
+    # Beyond 64 splits the last arrivals of every group of 16 splits each
+    # merge a slice of min(128, D) columns of one query head over all the
+    # set's partials (16 B per lane, 16 or 32 lanes per row slice); the sets
+    # here have G*D = 1024, 2048 or 4096 outputs, so 8 to 32 slices for 7
+    # or 16 groups.  With 250 splits the shorter sequence leaves most splits
+    # empty; the single-split output is the reference.
     c = DecodeCase(2, 2 * G, 2, D, [3000, 1777], "e4m3", seed=40 + D + G)
     ref, qheads = c.oracle()
     one = c.run_gpu(num_splits=1)

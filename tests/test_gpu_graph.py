@@ -1,6 +1,7 @@
 """Every entry point captured in a HIP graph (torch.cuda.CUDAGraph) and
 replayed: per-head scales, cache write, causal prefill, fused append + decode
-(one-level split merge) and plain decode (two-level split merge).
+(one merger per set) and plain decode (96 splits: the merge shared by the
+last arrivals of the split groups).
 
 The calls take their scales, lengths and inputs from device memory and
 allocate nothing, so a captured call replays with whatever those buffers hold.
@@ -136,7 +137,7 @@ def test_graph_replays_match_eager():
         _run(fa, x, graphed)
     torch.cuda.synchronize()
 
-    names = ["prefill out", "append+decode out", "two-level decode out", "k_scale", "v_scale",
+    names = ["prefill out", "append+decode out", "many-split decode out", "k_scale", "v_scale",
              "decode cache", "prefill cache"]
     for step in range(STEPS):
         log(f"[graph] step {step} lens={(np.asarray(BASE) + step + 1).tolist()}")

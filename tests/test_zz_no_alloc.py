@@ -45,9 +45,10 @@ def test_noalloc_equals_workspace_entry_point_on_consecutive_calls():
     small = DecodeCase(1, 8, 2, 64, [300], "e4m3", seed=81)
     _check(big, "llama-shaped batch 4")
     _check(small, "hd64 batch 1 (smaller layout)")
-    # 100 splits: grouped two-level merge with its second counter level
+    # 100 splits: arrivals counted per split group, the merge shared by the
+    # group finishers (the set and merger counters)
     two = DecodeCase(2, 16, 2, 256, [4000, 1777], "e5m2", seed=82)
-    _check(two, "hd256 two-level merge", num_splits=100)
+    _check(two, "hd256 sliced merge", num_splits=100)
     _check(small, "hd64 again after the two-level layout")
     _check(big, "llama-shaped again")
 
