@@ -155,7 +155,6 @@ constexpr int ws_vec(int cols, int nt) { return cols >= 4 * nt ? 4 : cols >= 2 *
 template <int D, int GW, int NW>
 __device__ __forceinline__ void merge_rows(const float* o_in, const float* m_in,
                                            const float* l_in, int n, float* o_dst, float vsc) {
-  const int rows = n, r0 = 0;
   constexpr int NT = 64 * NW;
   constexpr int V = ws_vec(GW * D, NT);               // columns per load
   constexpr int CG = GW * D / V;                      // V-column groups of the output
@@ -176,14 +175,14 @@ __device__ __forceinline__ void merge_rows(const float* o_in, const float* m_in,
   const int wave = t >> 6;
   const int col0 = t / R;
   const int r = t % R;
-  const __amdgpu_buffer_rsrc_t src = ws_rsrc(o_in, (uint32_t)(GW * rows * D * 4));
+  const __amdgpu_buffer_rsrc_t src = ws_rsrc(o_in, (uint32_t)(GW * n * D * 4));
 
   f32x4 v[EPT][JB];
   auto issue = [&](int j0) {
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
       const int col = col0 + e * (NT / R);
-      const uint32_t base = (uint32_t)((col / (D / V)) * rows + r0) * D + (col % (D / V)) * V;
+      const uint32_t base = (uint32_t)((col / (D / V)) * n) * D + (col % (D / V)) * V;
 #pragma unroll
       for (int j = 0; j < JB; ++j) {
         const int i = min(j0 + r + j * R, n - 1);   // rows past n repeat row n-1, weight 0
@@ -202,8 +201,8 @@ __device__ __forceinline__ void merge_rows(const float* o_in, const float* m_in,
     mv[k] = kNegInf;
     lv[k] = 0.f;
     if (i < GW * n) {
-      mv[k] = ld_agent(m_in + (size_t)(i / n) * rows + r0 + i % n);
-      lv[k] = ld_agent(l_in + (size_t)(i / n) * rows + r0 + i % n);
+      mv[k] = ld_agent(m_in + i);   // head i / n, row i % n
+      lv[k] = ld_agent(l_in + i);
     }
   }
   issue(0);

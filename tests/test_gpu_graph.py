@@ -26,7 +26,7 @@ B, HQ, HKV, D = 3, 32, 8, 128
 STEPS = 4
 BASE = [700, 1500, 2100]      # decode contexts before the first step
 P_LEN, P_Q = 1536, 512        # prefill sequence and its query chunk
-TWO_LEVEL_SPLITS = 96         # > 64 splits: group partials, then a final merge
+TWO_LEVEL_SPLITS = 96         # > 64 splits: group counters, merge shared by slices
 
 
 class Path:
