@@ -276,6 +276,11 @@ static fa8_status decode_impl(const void* q, int32_t batch, int32_t num_q_heads,
 
   const int S = num_splits > 0 ? num_splits
                                : fa8_decode_num_splits(batch, num_kv_heads, max_seq_len, window);
+  // Beyond kDecodeSingleLevel splits up to that many mergers of a set wait
+  // for the set's other splits, which must still find a CU to start on.
+  if (fa8::decode_num_groups(S) > 1 && device_cu_count() <= fa8::kDecodeSingleLevel)
+    return fail(FA8_EUNSUPPORTED, "decode: %d splits need more than %d compute units, the device has %d",
+                S, fa8::kDecodeSingleLevel, device_cu_count());
   fa8::DecodeParams p{};
   if (use_scratch) {
     const size_t cb = fa8::decode_counter_bytes(batch, num_q_heads, S);

@@ -317,8 +317,10 @@ __device__ __forceinline__ void merge_slice(const float* o_head, const float* m_
   f32x4 v[JR];
 #pragma unroll
   for (int j = 0; j < JR; ++j) {
-    const int i = min(rp + j * RP, n - 1);   // rows past n repeat row n-1, never used
-    v[j] = ld_agentv<4>(src, (uint32_t)(i * D + c0 + 4 * cg) * 4);
+    if (j * RP < n) {   // passes wholly past row n-1 load nothing
+      const int i = min(rp + j * RP, n - 1);   // rows past n repeat row n-1, never used
+      v[j] = ld_agentv<4>(src, (uint32_t)(i * D + c0 + 4 * cg) * 4);
+    }
   }
   for (int i = t; i < n; i += NT) {
     s_w[i] = ld_agent(m_head + i);

@@ -50,7 +50,7 @@ struct DecodeParams {
 // Splits are merged by the last workgroup to arrive when there are at most
 // kDecodeSingleLevel of them; beyond that, arrivals are counted per group of
 // kDecodeFan splits and the merge is spread over the last arrivals of every
-// group, one slice of 64 output columns each (decode.hip).
+// group, one slice of output columns each (decode.hip).
 constexpr int kDecodeMaxSplits = 256;
 constexpr int kDecodeSingleLevel = 64;
 constexpr int kDecodeFan = 16;

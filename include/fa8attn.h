@@ -170,6 +170,11 @@ size_t fa8_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
  *   window       > 0: attend to the last `window` keys (the query's own
  *                token included); <= 0: the whole context.
  *   num_splits   context splits, 0..256; 0 = fa8_decode_num_splits(...).
+ *                Beyond 64 splits up to 64 merging workgroups of a
+ *                (sequence, KV head) wait, with a bounded poll, for its
+ *                other splits: FA8_EUNSUPPORTED on a device with 64 or
+ *                fewer compute units (fa8_decode_num_splits never picks
+ *                more splits than there are compute units).
  *   out          fp32 [batch][num_q_heads][head_dim]
  *                out = sum_j softmax(sm_scale * q.K_j) * V_j.
  *   workspace    >= fa8_decode_workspace_bytes(batch, num_q_heads,
