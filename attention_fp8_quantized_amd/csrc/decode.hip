@@ -290,9 +290,10 @@ constexpr int kSliceCols = FA8_MERGE_SLICE_COLS;
 // wave owns the four columns 4 (l % CG) .. +3 (CG = SW / 4) of one
 // row, the wave's lanes covering 64 / CG consecutive rows, so that one load
 // instruction covers whole row slices (the loads bypass the caches: rows
-// scattered over the lanes would fetch each line several times).  All
-// partial loads are issued before the weights are waited for; the row sums
-// meet through lane shuffles and an LDS array.
+// scattered over the lanes would fetch each line several times).  The
+// maxima and denominators are loaded first and all partial loads are issued
+// before the weights are waited for; the row sums meet through lane shuffles
+// and an LDS array.
 template <int D, int NW, int SW>
 __device__ __forceinline__ void merge_slice(const float* o_head, const float* m_head,
                                             const float* l_head, int n, int c0,
@@ -314,17 +315,32 @@ __device__ __forceinline__ void merge_slice(const float* o_head, const float* m_
   const int cg = lane % CG;                           // four-column group
   const int rp = RW * wave + lane / CG;               // first row of the lane
   const __amdgpu_buffer_rsrc_t src = ws_rsrc(o_head, (uint32_t)(n * D * 4));
-  f32x4 v[JR];
+  // the maxima and denominators are requested first, so that only they are
+  // waited for before the weights; the partial rows stream in meanwhile
+  constexpr int ML = (kDecodeMaxSplits + NT - 1) / NT;
+  float mv[ML], lv[ML];
 #pragma unroll
-  for (int j = 0; j < JR; ++j) {
-    if (j * RP < n) {   // passes wholly past row n-1 load nothing
-      const int i = min(rp + j * RP, n - 1);   // rows past n repeat row n-1, never used
-      v[j] = ld_agentv<4>(src, (uint32_t)(i * D + c0 + 4 * cg) * 4);
+  for (int k = 0; k < ML; ++k) {
+    const int i = t + k * NT;
+    if (i < n) {
+      mv[k] = ld_agent(m_head + i);
+      lv[k] = ld_agent(l_head + i);
     }
   }
-  for (int i = t; i < n; i += NT) {
-    s_w[i] = ld_agent(m_head + i);
-    s_lw[i] = ld_agent(l_head + i);
+  // rows past n-1 lie beyond the buffer resource's range (n rows): those
+  // loads return zeros without a memory access, and no branch splits the
+  // batch, so the wait below covers only the maxima and denominators
+  f32x4 v[JR];
+#pragma unroll
+  for (int j = 0; j < JR; ++j)
+    v[j] = ld_agentv<4>(src, (uint32_t)((rp + j * RP) * D + c0 + 4 * cg) * 4);
+#pragma unroll
+  for (int k = 0; k < ML; ++k) {
+    const int i = t + k * NT;
+    if (i < n) {
+      s_w[i] = mv[k];
+      s_lw[i] = lv[k];
+    }
   }
   __syncthreads();
   if (t < 64) {   // one wave: the maximum, the weights and the denominator
