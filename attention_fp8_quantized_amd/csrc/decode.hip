@@ -410,14 +410,15 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast(bf16x8, w); }
 
 // Waves per SIMD the register budget is sized for, without spills: four at
-// head_dim 64, three at 128, two at 256.
-template <int D, int kFmt>
+// head_dim 64, three at 128 (two with 16 query heads per KV head, whose
+// merge state needs more), two at 256.
+template <int D, int G>
 constexpr int decode_min_waves() {
-  return D == 64 ? 4 : D == 128 ? 3 : 2;
+  return D == 64 ? 4 : D == 128 ? (G == 16 ? 2 : 3) : 2;
 }
 
 template <int D, int G, int kFmt, int NW, int PD>
-__global__ __launch_bounds__(64 * NW, (decode_min_waves<D, kFmt>())) void decode_split_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64 * NW, (decode_min_waves<D, G>())) void decode_split_kernel(DecodeParams p) {
   constexpr bool kFp8 = kFmt != kFmtBf16;
   constexpr int ES = kFp8 ? 1 : 2;       // bytes per element
   constexpr int ROW = D * ES;            // bytes per cached row
