@@ -121,6 +121,40 @@ def test_cache_write_rejects_bad_arguments(lib):
     assert lib.fa8_last_error() == b""
 
 
+
+@fake_pointers
+def test_last_error_is_per_thread(lib):
+    # one thread's failure message is not visible to, nor overwritten by,
+    # another thread's calls
+    import threading
+    fake = _p(0x1000)
+    gate1, gate2 = threading.Barrier(2), threading.Barrier(2)
+    seen = {}
+
+    def fail_dtype():
+        assert lib.fa8_cache_write(fake, fake, 2, 1, 1, 64, fake, fake, fake, fake, 2, 1, None) == EINVAL
+        gate1.wait()          # the other thread fails now
+        gate2.wait()
+        seen["a"] = lib.fa8_last_error()
+
+    def fail_head_dim():
+        gate1.wait()
+        assert lib.fa8_cache_write(fake, fake, 0, 1, 1, 96, fake, fake, fake, fake, 2, 1, None) == EUNSUPPORTED
+        seen["b"] = lib.fa8_last_error()
+        gate2.wait()
+
+    def clean():
+        seen["c"] = lib.fa8_last_error()
+
+    ts = [threading.Thread(target=f) for f in (fail_dtype, fail_head_dim, clean)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join(30)
+    assert b"in_dtype" in seen["a"] and b"96" not in seen["a"]
+    assert b"96" in seen["b"] and b"in_dtype" not in seen["b"]
+    assert seen["c"] == b""
+
 def _decode(lib, **over):
     fake = _p(0x1000)
     a = dict(q=fake, B=1, Hq=8, cache=fake, cd=2, nb=4, Hkv=2, D=64, bt=fake, mb=4,
