@@ -121,9 +121,11 @@ constexpr int kLgkm0 = 0xC07F;
 
 // MB = query blocks of 16 rows per wave; the workgroup has 8/MB waves and
 // always 128 query rows.  With MB = 2 each widened K operand and each V^T
-// operand feeds two MFMAs, and a wave owns a SIMD (up to 512 registers).
+// operand feeds two MFMAs.  At head_dim 128 a wave then fits in 256
+// registers, so two workgroups of four waves share a CU (two waves per
+// SIMD, as with MB = 1); at head_dim 256 it needs a whole SIMD.
 template <int D, int kFmt, bool kDeferred, int MB>
-__global__ __launch_bounds__(64 * (8 / MB)) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(64 * (8 / MB), (MB == 2 && D <= 128) ? 2 : 1) void prefill_kernel(PrefillParams p) {
   constexpr int NWV = 8 / MB;              // waves per workgroup
   constexpr int KQ = D / 32;               // 32-wide chunks of the head dim (bf16 MFMA K)
   constexpr int DB = D / 16;               // 16-wide output column blocks
@@ -565,26 +567,30 @@ __global__ __launch_bounds__(64 * (8 / MB)) void prefill_kernel(PrefillParams p)
     }
 }
 
-#ifndef FA8_PREFILL_MB
-#define FA8_PREFILL_MB 1       // query blocks of 16 rows per wave (1 or 2)
-#endif
+// Query blocks per wave by head_dim, measured on MI355X (32k causal chunk,
+// 8 query heads on one KV head, two-level / one-level accumulation): at 128
+// two blocks take 2.50 / 2.42-2.44 ms against 2.73 / 2.59 ms for one; at 64
+// one block is faster (1.80-1.84 / 1.73 ms against 1.86 / 1.77 ms); at 256
+// two blocks need a whole SIMD per wave and spill (8.3 ms against 4.3 ms).
+// Flush every N tiles keeps one block per wave (its second accumulator
+// already fills the registers).
+template <int D, bool kDeferred>
+constexpr int prefill_mb() {
+  return (!kDeferred && D == 128) ? 2 : 1;
+}
+
+template <int D, int kFmt, bool kDeferred>
+static void launch_prefill_d(const PrefillParams& p, dim3 grid, hipStream_t stream) {
+  constexpr int MB = prefill_mb<D, kDeferred>();
+  hipLaunchKernelGGL((prefill_kernel<D, kFmt, kDeferred, MB>), grid, dim3(64 * (8 / MB)), 0, stream, p);
+}
 
 template <int kFmt, bool kDeferred>
 static hipError_t launch_prefill_f(const PrefillParams& p, dim3 grid, hipStream_t stream) {
-  // flush every N tiles keeps one query block per wave (its second
-  // accumulator already fills the registers)
-  constexpr int MB = kDeferred ? 1 : FA8_PREFILL_MB;
-  const dim3 block(64 * (8 / MB));
   switch (p.head_dim) {
-    case 64:
-      hipLaunchKernelGGL((prefill_kernel<64, kFmt, kDeferred, MB>), grid, block, 0, stream, p);
-      break;
-    case 128:
-      hipLaunchKernelGGL((prefill_kernel<128, kFmt, kDeferred, MB>), grid, block, 0, stream, p);
-      break;
-    case 256:
-      hipLaunchKernelGGL((prefill_kernel<256, kFmt, kDeferred, MB>), grid, block, 0, stream, p);
-      break;
+    case 64: launch_prefill_d<64, kFmt, kDeferred>(p, grid, stream); break;
+    case 128: launch_prefill_d<128, kFmt, kDeferred>(p, grid, stream); break;
+    case 256: launch_prefill_d<256, kFmt, kDeferred>(p, grid, stream); break;
     default: return hipErrorNotSupported;
   }
   return hipGetLastError();
