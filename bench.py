@@ -29,6 +29,8 @@ Printed: one JSON line with
                 (two-level and one-level accumulation) against the 5 PFLOP/s
                 dense FP8 MFMA peak, a 128k fill in four 32k chunks, decode
                 at 128k
+  prefill_llama 32 q / 8 KV heads, head_dim 128: 32k causal FP8 prefill
+                chunk (two-level and one-level accumulation)
   cpu_baseline  the fp64 NumPy oracle decoding one layer of the headline
                 workload on the host cores (bounded sample)
 
@@ -498,6 +500,39 @@ def measure_hd256(fa, torch, reps=5, modes=(1, 0, 2, 4, 8)):
     return res
 
 
+def measure_prefill_llama(fa, torch, reps=5):
+    """Llama-3.1-8B-shaped causal FP8 prefill: 32 q / 8 KV heads, head_dim
+    128, one 32k chunk (P = 0), two-level and one-level accumulation."""
+    Hq, Hkv, D, T = 32, 8, 128, 32768
+    dev = torch.device("cuda")
+    nb = T // 16
+    cache, ks, vs = fill_pool(fa, torch, nb, Hkv, D, "e4m3", seed=5200, outliers=False)
+    bt = torch.randperm(nb, generator=torch.Generator().manual_seed(52)).to(torch.int32)
+    bt = bt.view(1, nb).cuda()
+    gq = torch.Generator(device=dev)
+    gq.manual_seed(5201)
+    q = torch.randn((T, Hq, D), generator=gq, device=dev).to(torch.bfloat16)
+    qs = (q.float().abs().amax() / 448.0).view(1).contiguous()
+    cu = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    lens = torch.tensor([T], dtype=torch.int32, device=dev)
+    out = torch.empty((T, Hq, D), dtype=torch.float32, device=dev)
+    sm = 1.0 / math.sqrt(D)
+    fl = prefill_flops(T, 0, Hq, D)
+    for _ in range(4):
+        fa.prefill_attention(q, cu, cache, bt, lens, qs, ks, vs, sm, T, out=out)
+    res = []
+    for mode in (1, 0):
+        ms = timed(torch, lambda: fa.prefill_attention(q, cu, cache, bt, lens, qs, ks, vs, sm, T,
+                                                       accum_mode=mode, out=out), reps)
+        tf = fl / (ms * 1e-3) / 1e12
+        res.append({"accum_mode": mode, "ms": round(ms, 4), "tflops": round(tf, 1),
+                    "frac_fp8_peak": round(tf / FP8_MFMA_PEAK_TFLOPS, 4)})
+        log(f"  llama prefill 32k accum_mode={mode}: {ms:.3f} ms, {tf:.0f} TFLOP/s")
+    del cache, out, q
+    torch.cuda.empty_cache()
+    return {"heads": "32 q / 8 KV, head_dim 128", "prefill_32k": res}
+
+
 def measure_e5m2(fa, torch, reps=3):
     """The e5m2 cache: decode of the 32k Llama-shaped layer (16 distinct
     layers per format, decode launches alone) and the causal hd-256 prefill
@@ -852,6 +887,8 @@ def main():
         log("head_dim 256")
         result["hd256"] = measure_hd256(
             fa, torch, modes=tuple(int(m) for m in args.accum_modes.split(",")))
+        log("Llama-shaped prefill")
+        result["prefill_llama"] = measure_prefill_llama(fa, torch)
         log("on-device absmax scales")
         result["absmax_scales"] = measure_absmax(fa, torch)
         result["cache_write_bulk"] = measure_cache_write_bulk(fa, torch)
