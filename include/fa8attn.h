@@ -13,8 +13,9 @@
  * Conventions shared by every call
  * --------------------------------
  * - Every pointer argument is a DEVICE pointer owned by the caller (normally
- *   the storage of a torch tensor).  The library allocates nothing and keeps
- *   no device state; scratch space for decode is a caller-sized workspace.
+ *   the storage of a torch tensor).  The library allocates nothing; scratch
+ *   space for decode is a caller-sized workspace (fa8_decode_attention_noalloc
+ *   uses a fixed array of the library's own instead, described there).
  * - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
  *   NULL = the null stream).  No call synchronises with the host or copies
  *   between host and device, so every call can be captured in a HIP graph.
