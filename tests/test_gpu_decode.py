@@ -202,6 +202,24 @@ def test_uniform_scores_give_mean_of_v():
         at += L
 
 
+def test_more_sets_than_compute_units():
+    # 40 sequences x 8 KV heads = 320 (sequence, KV head) sets: one split
+    # each, so the workgroups run in more than one round and write their rows
+    # straight from the wave merge; ragged lengths, one empty sequence
+    import attention_fp8_quantized_amd as fa
+    rng = np.random.default_rng(60)
+    lens = [int(x) for x in rng.integers(1, 600, size=40)]
+    lens[3] = 0
+    assert fa.decode_num_splits(40, 8, max(lens)) == 1
+    c = DecodeCase(40, 32, 8, 128, lens, "e4m3", seed=60)
+    got = _check(c, "40 sequences x 8 KV heads, one split")
+    assert np.all(got[3] == 0), "empty sequence must give zeros"
+    # and with explicit splits: 320 sets x 4 splits, four rounds of workgroups
+    got4 = c.run_gpu(num_splits=4)
+    ref, qheads = c.oracle()
+    assert_gate(got4[:, qheads], ref, "40 sequences x 8 KV heads, 4 splits")
+
+
 def test_loaded_decode_shape():
     # 8 sequences of U{18000..22000} tokens, 32 q / 8 KV heads, head_dim 128
     import workloads as W
