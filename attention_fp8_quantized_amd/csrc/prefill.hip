@@ -10,14 +10,16 @@
 // The cache holds e4m3 or e5m2 codes ([GPUSTACK] "KV キャッシュの量子化"
 // names both FP8 cache formats); the query and P are always e4m3.
 //
-// Work decomposition: one workgroup of 8 waves per (128 query rows, query
-// head, sequence); each wave owns 16 query rows.  Keys are visited in tiles
+// Work decomposition: one workgroup per (128 query rows, query head,
+// sequence); 8 waves of 16 query rows each, or at head_dim 128 4 waves of two
+// 16-row blocks each (see prefill_mb).  Keys are visited in tiles
 // of 128 at absolute, 128-aligned positions, in ascending order (this order
 // and width are part of the numeric contract, see fa8_prefill_kv_tile).
 //
 // Per KV tile:
 //   * the tile's K and V rows (8 pages of FP8 codes) are copied straight
-//     into LDS (global_load_lds, 16 bytes per lane) with the next tile's
+//     into LDS (buffer loads with an LDS destination, 16 bytes per lane)
+//     with the next tile's
 //     copies in flight during the current tile (two buffers); the block ids
 //     two tiles ahead are fetched meanwhile;
 //   * S^T = K . Q^T on v_mfma_f32_16x16x32_bf16: the A operand is 8 K codes
