@@ -18,10 +18,9 @@
 //
 // Per KV tile:
 //   * the tile's K and V rows (8 pages of FP8 codes) are copied straight
-//     into LDS (buffer loads with an LDS destination, 16 bytes per lane)
-//     with the next tile's
-//     copies in flight during the current tile (two buffers); the block ids
-//     two tiles ahead are fetched meanwhile;
+//     into LDS (buffer loads with an LDS destination, 16 bytes per lane),
+//     the next tile's copies in flight during the current tile (two
+//     buffers); the block ids two tiles ahead are fetched meanwhile;
 //   * S^T = K . Q^T on v_mfma_f32_16x16x32_bf16: the A operand is 8 K codes
 //     of one key row per lane, widened to bf16 after the LDS read (exact:
 //     bf16 holds every e4m3 and e5m2 value), the B operand the e4m3 query
