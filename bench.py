@@ -764,6 +764,8 @@ def main():
                     help="only the head_dim-256 leg (prefill + 128k decode); prints its JSON")
     ap.add_argument("--hybrid-only", action="store_true",
                     help="only the gpt-oss-20b-shaped hybrid leg; prints its JSON")
+    ap.add_argument("--llama-prefill-only", action="store_true",
+                    help="only the Llama-shaped head_dim-128 prefill leg; prints its JSON")
     ap.add_argument("--accum-modes", default="1,0,2,4,8",
                     help="prefill accumulation modes the head_dim-256 leg times (comma list)")
     args = ap.parse_args()
@@ -782,6 +784,9 @@ def main():
         return
     if args.hybrid_only:
         print(json.dumps({"hybrid": measure_hybrid(fa, torch)}), flush=True)
+        return
+    if args.llama_prefill_only:
+        print(json.dumps({"prefill_llama": measure_prefill_llama(fa, torch)}), flush=True)
         return
 
     B, Hq, Hkv, D, ctx, layers = 1, 32, 8, 128, args.ctx, args.layers
