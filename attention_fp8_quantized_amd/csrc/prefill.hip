@@ -143,7 +143,13 @@ __global__ __launch_bounds__(64 * (8 / MB), (MB == 2 && D <= 128) ? 2 : 1) void 
   // the other one is being computed on
   __shared__ __attribute__((aligned(16))) uint8_t s_buf0[2 * TILE];
   __shared__ __attribute__((aligned(16))) uint8_t s_buf1[2 * TILE];
-  __shared__ int s_bt[4][PPT];             // block ids of tiles t .. t+3 (ring)
+  // Block ids of the staged pages live in registers, except in the
+  // flush-every-N instantiation at head_dim 256: it spills, and the extra
+  // live register raised its spill from 124 to 156 bytes per lane (32k
+  // chunk with N = 2: 6.17 against 5.70 ms), so it keeps them in an LDS ring
+  // of tiles t .. t+3.
+  constexpr bool kIdRing = kDeferred && D == 256;
+  __shared__ int s_bt[kIdRing ? 4 : 1][PPT];
 
   const int hq = blockIdx.y;
   const int b = blockIdx.z;
@@ -258,7 +264,12 @@ __global__ __launch_bounds__(64 * (8 / MB), (MB == 2 && D <= 128) ? 2 : 1) void 
   // (first TILE bytes) or V tile, one 16-byte chunk per lane.  The row of a
   // lane within its page, and so its swizzle, depends on u at most through
   // u's parity: the two per-lane source offsets are computed once, and each
-  // copy adds the (uniform) page address.
+  // copy adds the (uniform) page address.  Lane j of a wave holds the block
+  // id of the page its copy j % NCOPY reads: the ids are loaded a tile ahead
+  // of their copies into registers and broadcast with readlane.  (With the
+  // LDS ring, thread j < PPT loads page j's id and stores it in the ring.)
+  const int cpage = kIdRing ? (int)(threadIdx.x % PPT)
+                            : (((lane % NCOPY) * NWV + wave) % CPT) * RPI / kBlockSize;
   int lane_off[2];
 #pragma unroll
   for (int par = 0; par < 2; ++par) {
@@ -271,7 +282,7 @@ __global__ __launch_bounds__(64 * (8 / MB), (MB == 2 && D <= 128) ? 2 : 1) void 
   // LDS through the flat aperture, they leave the compiler's LDS counter in
   // order, so an operand read waits for its own data only instead of for
   // every LDS read in flight.
-  auto stage = [&](uint8_t* buf, int slot) {
+  auto stage = [&](uint8_t* buf, int ids, int slot) {
     // opaque per call, so that the compiler keeps 32-bit lane offsets and
     // uniform page addresses instead of hoisting a 64-bit address per copy
     int voff0 = lane_off[0], voff1 = lane_off[1];
@@ -281,7 +292,8 @@ __global__ __launch_bounds__(64 * (8 / MB), (MB == 2 && D <= 128) ? 2 : 1) void 
       const int idx = u * NWV + wave;                    // 0 .. 2*CPT-1
       const int kv = idx / CPT;
       const int row0 = (idx % CPT) * RPI;                // first row (within the tile)
-      const int blk = __builtin_amdgcn_readfirstlane(s_bt[slot][row0 / kBlockSize]);
+      const int blk = kIdRing ? __builtin_amdgcn_readfirstlane(s_bt[slot][row0 / kBlockSize])
+                              : __builtin_amdgcn_readlane(ids, u);
       const uint8_t* page = p.cache + (size_t)blk * blk_stride + head_off +
                             (size_t)kv * kBlockSize * D;
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -293,12 +305,16 @@ __global__ __launch_bounds__(64 * (8 / MB), (MB == 2 && D <= 128) ? 2 : 1) void 
 
   // block ids of the first two tiles (pages below the window start read the
   // first visible page's entry instead)
-  if (threadIdx.x < 2 * PPT) {
-    const int t = t_lo + threadIdx.x / PPT;
-    s_bt[t & 3][threadIdx.x % PPT] = page_blk(max(t * PPT + threadIdx.x % PPT, lo_key / kBlockSize));
+  const int ids_first = page_blk(max(t_lo * PPT + cpage, lo_key / kBlockSize));
+  int ids_n1 = page_blk(max((t_lo + 1) * PPT + cpage, lo_key / kBlockSize));   // tile t+1
+  if constexpr (kIdRing) {
+    if (threadIdx.x < PPT) {
+      s_bt[t_lo & 3][threadIdx.x] = ids_first;
+      s_bt[(t_lo + 1) & 3][threadIdx.x] = ids_n1;
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  stage(s_buf0, t_lo & 3);
+  stage(s_buf0, ids_first, t_lo & 3);
   // A window that starts inside the first tile: its V rows before the first
   // visible key hold another page's rows or a stale page's bytes (NaN codes,
   // say), and P = 0 times NaN would be NaN.  Wait for this tile's copies and
@@ -325,14 +341,13 @@ __global__ __launch_bounds__(64 * (8 / MB), (MB == 2 && D <= 128) ? 2 : 1) void 
     uint8_t* nxt = kOdd ? s_buf0 : s_buf1;
     const uint8_t* s_k = cur;
     const uint8_t* s_v = cur + TILE;
-    // block ids of tile t+2 (every thread loads one, so that the number of
-    // copies in flight is the same in every lane)
-    const int nb_page = (t + 2) * PPT + (threadIdx.x % PPT);
-    const int next_blk = page_blk(nb_page);
+    // block ids of tile t+2 (every lane loads one, so that the number of
+    // loads in flight is the same in every lane)
+    const int ids_n2 = page_blk((t + 2) * PPT + cpage);
     // the next tile's copies (after the last tile: a tile past the end, all
     // zero rows, never read), then wait for this tile's copies: everything
     // but the id load and the NCOPY copies just issued
-    stage(nxt, (t + 1) & 3);
+    stage(nxt, ids_n1, (t + 1) & 3);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(NCOPY + 1));
     // rows past the sequence end (the tail tile only): they hold another
     // page's rows or whatever a stale page held, and P = 0 times NaN would
@@ -539,10 +554,20 @@ __global__ __launch_bounds__(64 * (8 / MB), (MB == 2 && D <= 128) ? 2 : 1) void 
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (threadIdx.x < PPT) s_bt[(t + 2) & 3][threadIdx.x] = next_blk;
+    ids_n1 = ids_n2;
     // every wave is done with this buffer (the next copies into it start
-    // after this barrier) and the block ids are visible
-    __syncthreads();
+    // after this barrier).  The fence covers LDS only, so the copies in
+    // flight into the other buffer stay in flight across the barrier (a
+    // full workgroup fence waits for every vector-memory operation).  With
+    // the LDS ring the barrier also publishes the block ids of tile t+2.
+    if constexpr (kIdRing) {
+      if (threadIdx.x < PPT) s_bt[(t + 2) & 3][threadIdx.x] = ids_n2;
+      __syncthreads();
+    } else {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    }
   };
 
   for (int t = t_lo; t <= t_hi; t += 2) {
