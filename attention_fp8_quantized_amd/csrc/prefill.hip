@@ -10,17 +10,20 @@
 // The cache holds e4m3 or e5m2 codes ([GPUSTACK] "KV キャッシュの量子化"
 // names both FP8 cache formats); the query and P are always e4m3.
 //
-// Work decomposition: one workgroup per (128 query rows, query head,
-// sequence); 8 waves of 16 query rows each, or at head_dim 128 4 waves of two
-// 16-row blocks each (see prefill_mb).  Keys are visited in tiles
+// Work decomposition: one workgroup per (query block, query head,
+// sequence): at head_dim 256 and 64, 64 query rows in 4 waves of 16 rows
+// (several workgroups per CU, one tile buffer each); at head_dim 128, 128
+// rows in 4 waves of two 16-row blocks; flushing every N tiles, 128 rows in
+// 8 waves of 16 (see prefill_mb and prefill_nwv).  Keys are visited in tiles
 // of 128 at absolute, 128-aligned positions, in ascending order (this order
 // and width are part of the numeric contract, see fa8_prefill_kv_tile).
 //
 // Per KV tile:
 //   * the tile's K and V rows (8 pages of FP8 codes) are copied straight
-//     into LDS (buffer loads with an LDS destination, 16 bytes per lane),
-//     the next tile's copies in flight during the current tile (two
-//     buffers); the block ids two tiles ahead are fetched meanwhile;
+//     into LDS (buffer loads with an LDS destination, 16 bytes per lane):
+//     with two buffers the next tile's copies are in flight during the
+//     current tile; with one, they start when every wave is done with it;
+//     the block ids two tiles ahead are fetched meanwhile;
 //   * S^T = K . Q^T on v_mfma_f32_16x16x32_bf16: the A operand is 8 K codes
 //     of one key row per lane, widened to bf16 after the LDS read (exact:
 //     bf16 holds every e4m3 and e5m2 value), the B operand the e4m3 query
@@ -59,7 +62,6 @@
 namespace fa8 {
 
 constexpr int kTileN = 128;      // keys per KV tile
-constexpr int kBlockM = 128;     // query rows per workgroup
 constexpr float kNegInfP = -__builtin_huge_valf();
 
 int prefill_kv_tile(int) { return kTileN; }
@@ -120,14 +122,20 @@ constexpr int vmcnt_imm(int n) { return 0x3F70 | (n & 15) | ((n >> 4) << 14); }
 // (vector-memory and exp counters not waited on)
 constexpr int kLgkm0 = 0xC07F;
 
-// MB = query blocks of 16 rows per wave; the workgroup has 8/MB waves and
-// always 128 query rows.  With MB = 2 each widened K operand and each V^T
-// operand feeds two MFMAs.  At head_dim 128 a wave then fits in 256
+// MB = query blocks of 16 rows per wave, NWV = waves per workgroup (16 MB
+// NWV = 64 or 128 query rows).  With MB = 2 each widened K operand and each
+// V^T operand feeds two MFMAs.  At head_dim 128 a wave then fits in 256
 // registers, so two workgroups of four waves share a CU (two waves per
-// SIMD, as with MB = 1); at head_dim 256 it needs a whole SIMD.
-template <int D, int kFmt, bool kDeferred, int MB>
-__global__ __launch_bounds__(64 * (8 / MB), (MB == 2 && D <= 128) ? 2 : 1) void prefill_kernel(PrefillParams p) {
-  constexpr int NWV = 8 / MB;              // waves per workgroup
+// SIMD, as with MB = 1); at head_dim 256 it needs a whole SIMD.  Four-wave
+// workgroups run two per CU (four at head_dim 64, 128 registers per lane).
+template <int D, int kFmt, bool kDeferred, int MB, int NWV>
+__global__ __launch_bounds__(64 * NWV, NWV == 4 ? (D == 64 ? 4 : 2) : 1) void prefill_kernel(PrefillParams p) {
+  constexpr int BM = 16 * MB * NWV;        // query rows per workgroup
+  // 64-row workgroups (two per CU at head_dim 256, four at 64) stage each
+  // tile into a single buffer once the tile before it is done; the other
+  // workgroups of the CU compute meanwhile, and their barriers are not the
+  // ones this workgroup waits at
+  constexpr bool kSB = BM == 64;
   constexpr int KQ = D / 32;               // 32-wide chunks of the head dim (bf16 MFMA K)
   constexpr int DB = D / 16;               // 16-wide output column blocks
   constexpr int TILE = kTileN * D;         // bytes of one staged K (or V) tile
@@ -138,11 +146,11 @@ __global__ __launch_bounds__(64 * (8 / MB), (MB == 2 && D <= 128) ? 2 : 1) void 
   static_assert(MB == 1 || MB == 2, "query blocks per wave");
   static_assert(!kDeferred || MB == 1, "flush every N tiles: one query block per wave");
   static_assert(NCOPY >= 1 && kBlockSize % RPI == 0 && NCOPY + 1 <= 63, "staging tiling");
-  static_assert(16 * MB * NWV == kBlockM, "rows per workgroup");
+  static_assert(BM == 64 || BM == 128, "rows per workgroup");
   // two tile buffers (K then V), filled by direct global->LDS copies while
   // the other one is being computed on
   __shared__ __attribute__((aligned(16))) uint8_t s_buf0[2 * TILE];
-  __shared__ __attribute__((aligned(16))) uint8_t s_buf1[2 * TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t s_buf1[kSB ? 16 : 2 * TILE];
   // Block ids of the staged pages live in registers, except in the
   // flush-every-N instantiation at head_dim 256: it spills, and the extra
   // live register raised its spill from 124 to 156 bytes per lane (32k
@@ -159,7 +167,7 @@ __global__ __launch_bounds__(64 * (8 / MB), (MB == 2 && D <= 128) ? 2 : 1) void 
   const int T = p.cu_q_lens[b + 1] - qs;
   // longest causal blocks first: block x of the grid takes query block
   // (gridDim.x - 1 - x)
-  const int q0 = (gridDim.x - 1 - blockIdx.x) * kBlockM;
+  const int q0 = (gridDim.x - 1 - blockIdx.x) * BM;
   if (q0 >= T) return;
   const int L = p.seq_lens[b];
   const int P0 = L - T;                    // position of the chunk's first query
@@ -210,7 +218,7 @@ __global__ __launch_bounds__(64 * (8 / MB), (MB == 2 && D <= 128) ? 2 : 1) void 
   const float qk = qsc * p.k_scale[h] * p.sm_scale * kLog2e;
 
   // ---- key range of this workgroup ---------------------------------------
-  const int rmax = min(q0 + kBlockM, T) - 1;
+  const int rmax = min(q0 + BM, T) - 1;
   const int lo_key = p.window > 0 ? max(0, P0 + q0 - p.window + 1) : 0;
   const int hi_key = P0 + rmax;
   const int t_lo = lo_key / kTileN;
@@ -337,8 +345,8 @@ __global__ __launch_bounds__(64 * (8 / MB), (MB == 2 && D <= 128) ? 2 : 1) void 
   // the other buffer than the one being read.
   auto tile_step = [&](auto odd_tag, int t) {
     constexpr bool kOdd = decltype(odd_tag)::value;
-    uint8_t* cur = kOdd ? s_buf1 : s_buf0;
-    uint8_t* nxt = kOdd ? s_buf0 : s_buf1;
+    uint8_t* cur = (kOdd && !kSB) ? s_buf1 : s_buf0;
+    uint8_t* nxt = (kOdd || kSB) ? s_buf0 : s_buf1;
     const uint8_t* s_k = cur;
     const uint8_t* s_v = cur + TILE;
     // block ids of tile t+2 (every lane loads one, so that the number of
@@ -347,8 +355,12 @@ __global__ __launch_bounds__(64 * (8 / MB), (MB == 2 && D <= 128) ? 2 : 1) void 
     // the next tile's copies (after the last tile: a tile past the end, all
     // zero rows, never read), then wait for this tile's copies: everything
     // but the id load and the NCOPY copies just issued
-    stage(nxt, ids_n1, (t + 1) & 3);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(NCOPY + 1));
+    if constexpr (!kSB) {
+      stage(nxt, ids_n1, (t + 1) & 3);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(NCOPY + 1));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(1));   // all but the id load
+    }
     // rows past the sequence end (the tail tile only): they hold another
     // page's rows or whatever a stale page held, and P = 0 times NaN would
     // be NaN, so every lane overwrites the V chunks it copied there with
@@ -426,7 +438,7 @@ __global__ __launch_bounds__(64 * (8 / MB), (MB == 2 && D <= 128) ? 2 : 1) void 
     __builtin_amdgcn_s_setprio(0);
     // tiles wholly visible to every row of the block skip the mask
     const int k_first = t * kTileN, k_last = k_first + kTileN - 1;
-    const bool full = k_last <= P0 + q0 && q0 + kBlockM <= T &&
+    const bool full = k_last <= P0 + q0 && q0 + BM <= T &&
                       (p.window <= 0 || P0 + rmax - k_first < p.window);
     i32x8 pa[MB];
     float alpha_o[MB][4];    // alpha of the four queries (4g + i) whose O rows this lane holds
@@ -554,6 +566,7 @@ __global__ __launch_bounds__(64 * (8 / MB), (MB == 2 && D <= 128) ? 2 : 1) void 
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    const int ids_n1_cur = ids_n1;
     ids_n1 = ids_n2;
     // every wave is done with this buffer (the next copies into it start
     // after this barrier).  The fence covers LDS only, so the copies in
@@ -568,12 +581,16 @@ __global__ __launch_bounds__(64 * (8 / MB), (MB == 2 && D <= 128) ? 2 : 1) void 
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     }
+    if constexpr (kSB) stage(nxt, ids_n1_cur, (t + 1) & 3);
   };
 
   for (int t = t_lo; t <= t_hi; t += 2) {
     tile_step(std::false_type{}, t);
     if (t + 1 <= t_hi) tile_step(std::true_type{}, t + 1);
   }
+  // the last tile's copies (a tile past the end) land before the waves end
+  // and the workgroup's LDS is released (s_endpgm would also wait for them)
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   if constexpr (kDeferred) flush_n();   // the tiles since the last flush
 
   // ---- epilogue: out = O * v_scale / l ---------------------------------------
@@ -605,10 +622,25 @@ constexpr int prefill_mb() {
   return (!kDeferred && D == 128) ? 2 : 1;
 }
 
+// Waves per workgroup.  Four-wave workgroups of one block per wave (64
+// rows, single tile buffer) at head_dim 256 and 64, measured on MI355X
+// against eight-wave double-buffered ones (32k chunk, 8 query heads on one
+// KV head): head_dim 256 4.01-4.07 / 3.84-3.99 ms against 4.20 / 4.10 ms
+// (two-level / one-level), head_dim 64 1.70-1.73 / 1.64 ms against
+// 1.77-1.81 / 1.69 ms (every 4 tiles 1.73 against 1.93 ms).  The head_dim
+// 256 flush-every-N instantiation spills more in that form (196 against 112
+// bytes per lane, 7.9 against 5.5 ms with N = 2) and keeps eight waves.
+template <int D, bool kDeferred>
+constexpr int prefill_nwv() {
+  return ((D == 256 && !kDeferred) || D == 64) ? 4 : 8 / prefill_mb<D, kDeferred>();
+}
+
 template <int D, int kFmt, bool kDeferred>
 static void launch_prefill_d(const PrefillParams& p, dim3 grid, hipStream_t stream) {
   constexpr int MB = prefill_mb<D, kDeferred>();
-  hipLaunchKernelGGL((prefill_kernel<D, kFmt, kDeferred, MB>), grid, dim3(64 * (8 / MB)), 0, stream, p);
+  constexpr int NWV = prefill_nwv<D, kDeferred>();
+  grid.x = (p.max_q_len + 16 * MB * NWV - 1) / (16 * MB * NWV);
+  hipLaunchKernelGGL((prefill_kernel<D, kFmt, kDeferred, MB, NWV>), grid, dim3(64 * NWV), 0, stream, p);
 }
 
 template <int kFmt, bool kDeferred>
@@ -623,7 +655,7 @@ static hipError_t launch_prefill_f(const PrefillParams& p, dim3 grid, hipStream_
 }
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
-  const dim3 grid((p.max_q_len + kBlockM - 1) / kBlockM, p.num_q_heads, p.batch);
+  const dim3 grid(1, p.num_q_heads, p.batch);   // x: query blocks, set per instantiation
   const bool deferred = p.accum_mode >= 2;
   switch (p.fmt) {
     case kFmtE4m3:

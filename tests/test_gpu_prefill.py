@@ -43,23 +43,26 @@ def test_single_chunk_all_rows(D, cd):
     log(f"  vs unquantised-P reference: max_abs={ma:.3e} rel_l2={rl:.3e}")
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("cd", ["e4m3", "e5m2"])
 @pytest.mark.parametrize("window", [0, 100])
-def test_chunked_ragged_batch_gqa(window, cd):
-    # three sequences: fresh (P=0), continued (P=300), short tail chunk
-    c = PrefillCase([130, 100, 17], [130, 400, 260], 8, 2, 128, seed=7, window=window,
+def test_chunked_ragged_batch_gqa(window, cd, D):
+    # three sequences: fresh (P=0), continued (P=300), short tail chunk; at
+    # head_dim 64 and 256 the workgroups hold 64 rows and one tile buffer
+    c = PrefillCase([130, 100, 17], [130, 400, 260], 8, 2, D, seed=7, window=window,
                     cache_dtype=cd)
-    log(f"prefill ragged window={window} cache={cd}")
+    log(f"prefill ragged window={window} cache={cd} D={D}")
     ref, slack = c.oracle()
-    assert_gate(c.run_gpu(), ref, f"ragged batch window={window} {cd}", slack=slack)
+    assert_gate(c.run_gpu(), ref, f"ragged batch window={window} {cd} D={D}", slack=slack)
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("cd", ["e4m3", "e5m2"])
-def test_stale_nan_rows_past_sequence_end(cd):
+def test_stale_nan_rows_past_sequence_end(cd, D):
     # pages are pre-filled with NaN codes (0xFF in both FP8 formats); the rows
     # past each sequence end keep them and must not reach the output
-    c = PrefillCase([130, 75], [130, 333], 4, 2, 128, seed=8, fill=0xFF, cache_dtype=cd)
-    log(f"prefill stale NaN rows cache={cd}")
+    c = PrefillCase([130, 75], [130, 333], 4, 2, D, seed=8, fill=0xFF, cache_dtype=cd)
+    log(f"prefill stale NaN rows cache={cd} D={D}")
     got = c.run_gpu()
     assert np.all(np.isfinite(got))
     ref, slack = c.oracle()
