@@ -45,12 +45,6 @@
 #include "fa8_device.hpp"
 #include "fa8_internal.hpp"
 
-// FP8 caches: P enters the P.V product as an f16 high and low part (1) or
-// as one f16 value (0).
-#ifndef FA8_DECODE_P_SPLIT
-#define FA8_DECODE_P_SPLIT 1
-#endif
-
 namespace fa8 {
 
 constexpr float kNegInf = -__builtin_huge_valf();
@@ -271,15 +265,12 @@ __device__ __forceinline__ void merge_rows(const float* o_in, const float* m_in,
 // came).
 constexpr int kMergeWaitPolls = 1 << 20;
 
-#ifndef FA8_MERGE_SLICE_COLS
-#define FA8_MERGE_SLICE_COLS 128
-#endif
 // Output columns per slice merger (a power of two from 16 to 256; capped at
 // head_dim).  Measured on MI355X, single-KV-head head_dim-256 layer with 8
 // query heads and 256 splits, 128k / 32k context: 16 columns 23.64 / 15.85
 // us, 32: 22.60 / 14.66, 64: 22.08 / 14.05, 128: 21.77 / 13.80 (16
 // mergers, one per split group), 256: 23.50 / 15.68.
-constexpr int kSliceCols = FA8_MERGE_SLICE_COLS;
+constexpr int kSliceCols = 128;
 
 // Merge all n (<= kDecodeMaxSplits) partial rows of one query head over the
 // SW output columns c0 .. c0+SW-1, run by one workgroup of NW waves:
@@ -661,10 +652,8 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, G>())) void decode_sp
       // p = hi + lo, both f16 (together 22 significant bits; V is exact in
       // f16, so each product pair carries p to about 2^-22)
       const f16x4 pa = {(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
-#if FA8_DECODE_P_SPLIT
       const f16x4 pl = {(_Float16)(pr[0] - (float)pa[0]), (_Float16)(pr[1] - (float)pa[1]),
                         (_Float16)(pr[2] - (float)pa[2]), (_Float16)(pr[3] - (float)pa[3])};
-#endif
 #pragma unroll
       for (int hh = 0; hh < NL; ++hh) {
         *reinterpret_cast<uint4*>(sv + n * RS + 16 * g) = pg.v[hh];
@@ -682,9 +671,7 @@ __global__ __launch_bounds__(64 * NW, (decode_min_waves<D, G>())) void decode_sp
           const f16x4 vb = {v01[0], v01[1], v23[0], v23[1]};
           f32x4 acc = o[hh * BPS + cb];
           acc = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vb, acc, 0, 0, 0);
-#if FA8_DECODE_P_SPLIT
           acc = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, vb, acc, 0, 0, 0);
-#endif
           o[hh * BPS + cb] = acc;
         }
       }
@@ -957,18 +944,9 @@ void decode_workspace_carve(void* ws, int batch, int num_q_heads, int head_dim, 
 // 32k 19.80 -> 19.36 us, 128k 55.08 -> 53.45 us, 8 x 20k 64.45 -> 62.80 us
 // (8k 11.15 -> 11.28 us).  A deeper ring at head_dim 64 (3 or 4 pages)
 // measured 5-6% slower.
-#ifndef FA8_DECODE_PIPE_64
-#define FA8_DECODE_PIPE_64 2
-#endif
-#ifndef FA8_DECODE_PIPE_128
-#define FA8_DECODE_PIPE_128 1
-#endif
-#ifndef FA8_DECODE_PIPE_256
-#define FA8_DECODE_PIPE_256 1
-#endif
 template <int D>
 constexpr int decode_pipe() {
-  return D == 64 ? FA8_DECODE_PIPE_64 : D == 128 ? FA8_DECODE_PIPE_128 : FA8_DECODE_PIPE_256;
+  return D == 64 ? 2 : 1;
 }
 
 template <int D, int G, int kFmt>

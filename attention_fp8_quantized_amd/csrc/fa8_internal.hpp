@@ -63,14 +63,8 @@ inline int decode_num_groups(int splits) {
 // merger counters), each kCounterStride ints apart (zero before the first
 // call; every call leaves them zero), then fp32 o_part [B][Hq][S][D], m and
 // l [B][Hq][S].  Every array starts 16-byte aligned when the workspace does.
-#ifndef FA8_COUNTER_STRIDE
-#define FA8_COUNTER_STRIDE 64
-#endif
-constexpr int kCounterStride = FA8_COUNTER_STRIDE;   // ints per counter (256 bytes)
-#ifndef FA8_DECODE_WAVES
-#define FA8_DECODE_WAVES 8
-#endif
-constexpr int kDecodeWaves = FA8_DECODE_WAVES;   // waves per decode workgroup
+constexpr int kCounterStride = 64;   // ints per counter (256 bytes: one line each)
+constexpr int kDecodeWaves = 8;      // waves per decode workgroup
 size_t decode_workspace_bytes(int batch, int num_q_heads, int head_dim, int splits);
 void decode_workspace_carve(void* ws, int batch, int num_q_heads, int head_dim, int splits,
                             DecodeParams& p);
