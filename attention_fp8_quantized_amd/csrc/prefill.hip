@@ -147,8 +147,8 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? (D == 64 ? 4 : 2) : 1) void pr
   static_assert(!kDeferred || MB == 1, "flush every N tiles: one query block per wave");
   static_assert(NCOPY >= 1 && kBlockSize % RPI == 0 && NCOPY + 1 <= 63, "staging tiling");
   static_assert(BM == 64 || BM == 128, "rows per workgroup");
-  // two tile buffers (K then V), filled by direct global->LDS copies while
-  // the other one is being computed on
+  // tile buffers (K then V), filled by direct global->LDS copies: two, one
+  // filled while the other is computed on, or (kSB) one
   __shared__ __attribute__((aligned(16))) uint8_t s_buf0[2 * TILE];
   __shared__ __attribute__((aligned(16))) uint8_t s_buf1[kSB ? 16 : 2 * TILE];
   // Block ids of the staged pages live in registers, except in the
