@@ -127,9 +127,11 @@ constexpr int kLgkm0 = 0xC07F;
 // V^T operand feeds two MFMAs.  At head_dim 128 a wave then fits in 256
 // registers, so two workgroups of four waves share a CU (two waves per
 // SIMD, as with MB = 1); at head_dim 256 it needs a whole SIMD.  Four-wave
-// workgroups run two per CU (four at head_dim 64, 128 registers per lane).
+// workgroups run two per CU (four at head_dim 64).  The register budget is
+// two waves per SIMD (256 registers per lane), four at head_dim 64 (128).
 template <int D, int kFmt, bool kDeferred, int MB, int NWV>
-__global__ __launch_bounds__(64 * NWV, NWV == 4 ? (D == 64 ? 4 : 2) : 1) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2, D == 64 ? 4 : 2)))
+void prefill_kernel(PrefillParams p) {
   constexpr int BM = 16 * MB * NWV;        // query rows per workgroup
   // 64-row workgroups (two per CU at head_dim 256, four at 64) stage each
   // tile into a single buffer once the tile before it is done; the other
