@@ -14,32 +14,35 @@ shapes the GPU tests use, that
   score masked, before it meets the P.V product.
 
 The model follows the kernel source (csrc/prefill.hip): grid
-(ceil(max_q_len/128), H_q, B), blocks dispatched longest-first, key range
-[lo_key, hi_key] per workgroup, tiles t_lo .. t_hi, block ids of tiles t_lo
-and t_lo+1 before the loop (clamped below to the window's first page) and of
-tile t+2 inside step t (clamped at the end only), staged copies of tile t+1
-inside step t (so one tile past t_hi is staged and never read), V rows
-zeroed before the window start in the prologue and past the end in the
-tail tile.
+(ceil(max_q_len/BM), H_q, B) with BM = 64 or 128 query rows per workgroup,
+blocks dispatched longest-first, key range [lo_key, hi_key] per workgroup,
+tiles t_lo .. t_hi, block ids of tiles t_lo and t_lo+1 before the loop
+(clamped below to the window's first page) and of tile t+2 inside step t
+(clamped at the end only), staged copies of tile t+1 inside step t (at its
+start with two tile buffers, at its end with one; either way one tile past
+t_hi is staged and never read), V rows zeroed before the window start in the
+prologue and past the end in the tail tile.  It also checks that the block
+id a lane holds is the one its wave's copy of the same index needs, for the
+workgroup shapes the launcher picks.
 """
 
 import pytest
 
 KV_TILE = 128
 BLOCK = 16
-BLOCK_M = 128
+BLOCK_MS = (64, 128)   # query rows per workgroup (head_dim 256 and 64: 64)
 
 
-def workgroups(q_len, seq_len, window, max_q_len):
+def workgroups(q_len, seq_len, window, max_q_len, block_m=128):
     """(q0, lo_key, hi_key, t_lo, t_hi) of every workgroup that does work."""
     out = []
-    nx = (max_q_len + BLOCK_M - 1) // BLOCK_M
+    nx = (max_q_len + block_m - 1) // block_m
     P0 = seq_len - q_len
     for x in range(nx):
-        q0 = (nx - 1 - x) * BLOCK_M
+        q0 = (nx - 1 - x) * block_m
         if q0 >= q_len:
             continue
-        rmax = min(q0 + BLOCK_M, q_len) - 1
+        rmax = min(q0 + block_m, q_len) - 1
         lo_key = max(0, P0 + q0 - window + 1) if window > 0 else 0
         hi_key = P0 + rmax
         out.append((q0, lo_key, hi_key, lo_key // KV_TILE, hi_key // KV_TILE))
@@ -107,23 +110,25 @@ for w in (100, 128, 513):
     SHAPES.append(([300, 129], [2000, 4096], w))
 
 
+@pytest.mark.parametrize("block_m", BLOCK_MS)
 @pytest.mark.parametrize("q_lens,seq_lens,window", SHAPES)
-def test_block_table_reads_stay_in_window(q_lens, seq_lens, window):
+def test_block_table_reads_stay_in_window(q_lens, seq_lens, window, block_m):
     max_q = max(q_lens)
     for T, L in zip(q_lens, seq_lens):
         lo_seq = max(0, L - T - window + 1) if window > 0 else 0
         n_pages = (L + BLOCK - 1) // BLOCK
-        for q0, lo_key, hi_key, t_lo, t_hi in workgroups(T, L, window, max_q):
+        for q0, lo_key, hi_key, t_lo, t_hi in workgroups(T, L, window, max_q, block_m):
             idx = entries_read(L, lo_key, t_lo, t_hi)
             assert min(idx) >= lo_seq // BLOCK, (T, L, window, q0, sorted(idx)[:4])
             assert max(idx) <= n_pages - 1, (T, L, window, q0)
 
 
+@pytest.mark.parametrize("block_m", BLOCK_MS)
 @pytest.mark.parametrize("q_lens,seq_lens,window", SHAPES)
-def test_invisible_staged_rows_are_zeroed(q_lens, seq_lens, window):
+def test_invisible_staged_rows_are_zeroed(q_lens, seq_lens, window, block_m):
     max_q = max(q_lens)
     for T, L in zip(q_lens, seq_lens):
-        for q0, lo_key, hi_key, t_lo, t_hi in workgroups(T, L, window, max_q):
+        for q0, lo_key, hi_key, t_lo, t_hi in workgroups(T, L, window, max_q, block_m):
             for t in range(t_lo, t_hi + 1):
                 assert zeroed_or_visible(L, lo_key, hi_key, t) == [], (T, L, window, q0, t)
 
@@ -142,3 +147,32 @@ def test_model_sees_the_old_clamp_fail():
             page = (t_lo + i // ppt) * ppt + i % ppt
             old.add(page if page < n_pages else 0)
     assert min(old) < lo_seq // BLOCK
+
+
+# (head_dim, query blocks per wave, waves per workgroup) of every prefill
+# instantiation: prefill_mb and prefill_nwv, two-level/one-level then
+# flush every N tiles
+LAUNCH_SHAPES = [(256, 1, 4), (128, 2, 4), (64, 1, 4), (256, 1, 8), (128, 1, 8)]
+
+
+@pytest.mark.parametrize("D,MB,NWV", LAUNCH_SHAPES)
+def test_lane_block_ids_match_the_copies(D, MB, NWV):
+    # copy u of wave w stages rows (idx % CPT) * RPI .. of the K (idx < CPT)
+    # or V tile, idx = u * NWV + w; lane j holds the id of page
+    # ((j % NCOPY) * NWV + w) % CPT * RPI / 16 and copy u broadcasts lane u's
+    tile = KV_TILE * D
+    rpi = 1024 // D
+    cpt = tile // 1024
+    ncopy = 2 * cpt // NWV
+    assert 16 * MB * NWV in BLOCK_MS and ncopy >= 1 and BLOCK % rpi == 0
+    staged = set()
+    for w in range(NWV):
+        lane_page = [((j % ncopy) * NWV + w) % cpt * rpi // BLOCK for j in range(64)]
+        for u in range(ncopy):
+            idx = u * NWV + w
+            assert idx < 2 * cpt
+            row0 = (idx % cpt) * rpi
+            assert lane_page[u] == row0 // BLOCK, (D, NWV, w, u)
+            staged |= {(idx // cpt, row0 + r) for r in range(rpi)}
+    # the copies of all waves cover every row of the K and V tiles once
+    assert staged == {(kv, r) for kv in (0, 1) for r in range(KV_TILE)}
