@@ -57,6 +57,28 @@ def test_chunked_ragged_batch_gqa(window, cd, D):
 
 
 @pytest.mark.parametrize("D", [64, 128, 256])
+def test_chunk_lengths_around_workgroup_rows(D):
+    # chunk lengths one below, at and one above the 64- and 128-row query
+    # blocks, fresh and continued sequences
+    c = PrefillCase([63, 64, 65, 127, 128, 129], [63, 200, 65, 300, 128, 700], 4, 2, D,
+                    seed=80 + D)
+    log(f"prefill chunk lengths around the query blocks D={D}")
+    ref, slack = c.oracle()
+    assert_gate(c.run_gpu(), ref, f"chunk lengths around the query blocks D={D}", slack=slack)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("window", [0, 100])
+def test_one_and_two_query_chunks(D, window):
+    # a chunk of one or two queries deep in its sequence: one query block,
+    # nearly all of its rows past the chunk end
+    c = PrefillCase([1, 1, 2], [1, 517, 260], 4, 2, D, seed=90 + D + window, window=window)
+    log(f"prefill one- and two-query chunks D={D} window={window}")
+    ref, slack = c.oracle()
+    assert_gate(c.run_gpu(), ref, f"one- and two-query chunks D={D} window={window}", slack=slack)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("cd", ["e4m3", "e5m2"])
 def test_stale_nan_rows_past_sequence_end(cd, D):
     # pages are pre-filled with NaN codes (0xFF in both FP8 formats); the rows
