@@ -538,20 +538,34 @@ void prefill_kernel(PrefillParams p) {
         since = 0;
       }
     } else if (p.accum_mode == 1) {
+      // level 1: this tile's P.V of a 16-column block into a zeroed
+      // accumulator; level 2: the fp32 flush O = alpha*O + acc, one block
+      // behind, so that the flush's wait for its product overlaps the next
+      // block's product (measured on MI355X, 32k chunk: head_dim 256 3.95 ->
+      // 3.90 ms, 128 2.39 -> 2.34 ms, 64 1.72 -> 1.69 ms)
       i32x8 vb_next = load_vb(0);
+      f32x4 acc_prev[MB];
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const i32x8 vb = vb_next;
         if (db + 1 < DB) vb_next = load_vb(db + 1);
-        // level 1: this tile's P.V into a zeroed accumulator; level 2: fp32 flush
+        f32x4 acc[MB];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const f32x4 acc = mfma_pv<kFmt>(pa[mb], vb, f32x4{0.f, 0.f, 0.f, 0.f});
+        for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma_pv<kFmt>(pa[mb], vb, f32x4{0.f, 0.f, 0.f, 0.f});
+        if (db > 0) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) o[mb][db][i] = alpha_o[mb][i] * o[mb][db][i] + acc[i];
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[mb][db - 1][i] = alpha_o[mb][i] * o[mb][db - 1][i] + acc_prev[mb][i];
         }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc_prev[mb] = acc[mb];
         __builtin_amdgcn_sched_barrier(0);
       }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[mb][DB - 1][i] = alpha_o[mb][i] * o[mb][DB - 1][i] + acc_prev[mb][i];
     } else {
       i32x8 vb_next = load_vb(0);
 #pragma unroll
