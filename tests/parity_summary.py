@@ -1,7 +1,7 @@
 """Markdown table of the parity records the GPU tests write.
 
-    FA8_PARITY_LOG=gpurun_out/parity.jsonl python -m pytest tests -m gpu
-    python tests/parity_summary.py gpurun_out/parity.jsonl
+    FA8_PARITY_LOG=/tmp/parity.jsonl python -m pytest tests -m gpu
+    python tests/parity_summary.py /tmp/parity.jsonl
 
 Prints, for every gated comparison that carries a context length (decode
 at 1k..128k, prefill chunks up to the last 32k chunk of a 128k fill, both
@@ -45,4 +45,4 @@ def table(recs):
 
 
 if __name__ == "__main__":
-    print(table(rows(sys.argv[1] if len(sys.argv) > 1 else "gpurun_out/parity.jsonl")))
+    print(table(rows(sys.argv[1] if len(sys.argv) > 1 else "parity.jsonl")))
